@@ -1,0 +1,411 @@
+"""Pins for the CPU oracle: brute force, closed forms, library routines and
+the values the pages print.  CPU only (no GPU marker)."""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tensor_gemm_reduce_lds_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_f32(rng, shape, lo=-1.0, hi=1.0):
+    return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+# ---------------------------------------------------------------- bf16 RNE
+def test_bf16_rne_ties_and_near_ties():
+    # 0x3F808000 sits exactly between 0x3F80 and 0x3F81: ties to even (0x3F80)
+    # 0x3F818000 sits between 0x3F81 and 0x3F82: ties to even (0x3F82)
+    # 0xBF808000 is the negative tie: ties to even magnitude (0xBF80)
+    # 0x3F808008 is just above the tie: rounds up (0x3F81)
+    bits = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F808008,
+                     0x3F807FFF, 0x00000000, 0x80000000], dtype=np.uint32)
+    got = O.bf16_rne(bits.view(np.float32))
+    assert got.tolist() == [0x3F80, 0x3F82, 0xBF80, 0x3F81, 0x3F80, 0, 0x8000]
+
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    # add specials: +-inf, largest finite (rounds to inf), denormals, ties
+    extra = np.array([0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x00000001,
+                      0x00008000, 0x00018000, 0x7F7F8000, 0x7F7F7FFF],
+                     dtype=np.uint32)
+    bits = np.concatenate([bits, extra])
+    x = bits.view(np.float32)
+    got = O.bf16_rne(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN stays NaN
+    back = (got[nan].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(back))
+
+
+# -------------------------------------------------------- reference values
+def _brute_force(A, B, C, alpha, beta, ldc):
+    """Exact rational arithmetic, straight from the definition:
+    out[i][j] = alpha * sum_r sum_k A_r[i][k] B_r[k][j] + beta * C[i][j]."""
+    W, M, K = A.shape
+    N = B.shape[2]
+    out = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for r in range(W):
+                for k in range(K):
+                    s += Fraction(float(A[r, i, k])) * Fraction(float(B[r, k, j]))
+            v = Fraction(alpha) * s
+            if C is not None:
+                c = C[j] if ldc == 0 else C[i, j]
+                v += Fraction(beta) * Fraction(float(c))
+            out[i, j] = v
+    return out
+
+
+@pytest.mark.parametrize("ldc_mode", ["none", "broadcast", "full"])
+def test_reference_brute_force_tiny(ldc_mode):
+    rng = np.random.default_rng(2)
+    W, M, K, N = 2, 4, 5, 3
+    A = _rand_f32(rng, (W, M, K))
+    B = _rand_f32(rng, (W, K, N))
+    C, ldc = None, 0
+    if ldc_mode == "broadcast":
+        C = _rand_f32(rng, (N,))
+    elif ldc_mode == "full":
+        C, ldc = _rand_f32(rng, (M, N)), N
+    alpha, beta = 0.75, -1.25
+    got = O.reference_rows(A, B, C, dtype=O.F32, alpha=alpha, beta=beta, ldc=ldc)
+    exact = _brute_force(A, B, C, alpha, beta, ldc)
+    for i, j in itertools.product(range(M), range(N)):
+        assert abs(Fraction(got[i, j]) - exact[i, j]) <= Fraction(1, 10**12)
+    # the element-wise entry point gives the same numbers
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    e = O.reference_elems(A, B, C, dtype=O.F32, alpha=alpha, beta=beta,
+                          ldc=ldc, ii=ii.ravel(), jj=jj.ravel())
+    np.testing.assert_allclose(e, got.ravel(), rtol=1e-13, atol=1e-13)
+
+
+def test_reference_exact_on_small_integers():
+    # integer inputs: fp64 is exact, so the oracle must equal integer math
+    rng = np.random.default_rng(3)
+    W, M, K, N = 3, 6, 7, 5
+    A = rng.integers(-3, 4, size=(W, M, K)).astype(np.float32)
+    B = rng.integers(-3, 4, size=(W, K, N)).astype(np.float32)
+    got = O.reference_rows(A, B, dtype=O.F32)
+    Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+    ref = sum(Ai[r] @ Bi[r] for r in range(W))
+    assert np.array_equal(got, ref.astype(np.float64))
+
+
+def test_sum_of_partials_equals_full_gemm():
+    # sum_r A_r B_r == [A_0 .. A_{W-1}] (along K) @ [B_0; ..; B_{W-1}] (along K)
+    rng = np.random.default_rng(4)
+    W, M, K, N = 4, 8, 16, 12
+    A = _rand_f32(rng, (W, M, K))
+    B = _rand_f32(rng, (W, K, N))
+    alpha = 1.5
+    got = O.reference_rows(A, B, dtype=O.F32, alpha=alpha)
+    A_full = np.concatenate([A[r] for r in range(W)], axis=1).astype(np.float64)
+    B_full = np.concatenate([B[r] for r in range(W)], axis=0).astype(np.float64)
+    np.testing.assert_allclose(got, alpha * (A_full @ B_full), rtol=1e-12, atol=1e-12)
+
+
+def test_w1_bf16_is_plain_gemm():
+    rng = np.random.default_rng(5)
+    M, K, N = 16, 64, 24
+    A = I.to_bf16_bits(rng.standard_normal((1, M, K)).astype(np.float32))
+    B = I.to_bf16_bits(rng.standard_normal((1, K, N)).astype(np.float32))
+    got = O.reference_rows(A, B, dtype=O.BF16)
+    Af = I.bf16_bits_to_f32(A[0]).astype(np.float64)
+    Bf = I.bf16_bits_to_f32(B[0]).astype(np.float64)
+    np.testing.assert_allclose(got, Af @ Bf, rtol=1e-12, atol=1e-12)
+
+
+def test_partials_are_rank_products():
+    rng = np.random.default_rng(6)
+    W, M, K, N = 4, 8, 8, 6
+    A = _rand_f32(rng, (W, M, K))
+    B = _rand_f32(rng, (W, K, N))
+    for r in range(W):
+        got = O.partial_rows(A, B, dtype=O.F32, alpha=-2.0, r=r)
+        ref = -2.0 * (A[r].astype(np.float64) @ B[r].astype(np.float64))
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("ldc", [0, 6])
+def test_bias_added_once_by_chunk_owner(ldc):
+    W, M, K, N = 4, 8, 3, 6     # Mc = 2
+    A = np.zeros((W, M, K), dtype=np.float32)
+    B = np.ones((W, K, N), dtype=np.float32)
+    rng = np.random.default_rng(7)
+    C = _rand_f32(rng, (N,) if ldc == 0 else (M, ldc))
+    beta = 0.5
+    Cm = np.broadcast_to(C, (M, N)) if ldc == 0 else C[:, :N]
+    out = O.reference_rows(A, B, C, dtype=O.F32, beta=beta, ldc=ldc)
+    np.testing.assert_array_equal(out, beta * Cm.astype(np.float64))
+    for r in range(W):
+        p = O.partial_rows(A, B, C, dtype=O.F32, beta=beta, ldc=ldc, r=r)
+        for i in range(M):
+            expect = beta * Cm[i].astype(np.float64) if i // 2 == r else 0.0
+            np.testing.assert_array_equal(p[i], np.broadcast_to(expect, (N,)))
+
+
+def test_alpha0_beta1_returns_c_bits():
+    rng = np.random.default_rng(8)
+    W, M, K, N = 4, 8, 64, 16
+    A = I.to_bf16_bits(rng.standard_normal((W, M, K)).astype(np.float32))
+    B = I.to_bf16_bits(rng.standard_normal((W, K, N)).astype(np.float32))
+    C = I.to_bf16_bits(rng.standard_normal((N,)).astype(np.float32))
+    got = O.emulate_rows(A, B, C, dtype=O.BF16, alpha=0.0, beta=1.0, ldc=0)
+    assert np.array_equal(got, np.broadcast_to(C, (M, N)))
+
+
+# ------------------------------------------------------------ reduce order
+def _order_case(dtype):
+    # rank r's partial at every element is v[r]: A_r = v[r] (K = 1), B_r = 1
+    v = np.array([2.0**24, 1, 1, 1, 1, 1, 1, -2.0**24], dtype=np.float32)
+    W, M, K, N = 8, 8, 1, 4
+    A = np.broadcast_to(v[:, None, None], (W, M, K)).astype(np.float32)
+    B = np.ones((W, K, N), dtype=np.float32)
+    if dtype == O.BF16:
+        A, B = I.to_bf16_bits(A), I.to_bf16_bits(B)
+    return v, A, B
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+def test_reduce_order_closed_form(dtype):
+    # float: 2^24 + 1 == 2^24 (tie to even), so the flat ascending sum loses
+    # every +1 and ends at 0; the two-level order keeps 1+1+1 in group 1 and
+    # ends at 3; the exact sum is 6.
+    v, A, B = _order_case(dtype)
+    ref = O.reference_rows(A, B, dtype=dtype)
+    assert np.all(ref == 6.0)
+    flat = O.emulate_rows(A, B, dtype=dtype, order=O.FLAT)
+    two = O.emulate_rows(A, B, dtype=dtype, order=O.TWO_LEVEL, groups=2)
+    if dtype == O.BF16:
+        flat, two = O.bf16_bits_to_f64(flat), O.bf16_bits_to_f64(two)
+    assert np.all(flat == 0.0) and np.all(two == 3.0)
+    S = np.broadcast_to(v[:, None], (8, 5)).astype(np.float32)
+    assert np.all(O.reduce_emulate(S, order=O.FLAT) == 0)
+    assert np.all(O.reduce_emulate(S, order=O.TWO_LEVEL, groups=2) == 0x4040)
+    assert np.all(O.reduce_emulate(S, order=O.TWO_LEVEL, groups=2,
+                                   out_bf16=False) == 3.0)
+    # G = 1 and G = W are both the flat ascending order
+    assert np.all(O.reduce_emulate(S, order=O.TWO_LEVEL, groups=1) == 0)
+    assert np.all(O.reduce_emulate(S, order=O.TWO_LEVEL, groups=8) == 0)
+    # G = 4: (2^24+1) + (1+1) + (1+1) + (1-2^24) -> 2^24 + 2 + 2 - (2^24-1) = 5
+    assert np.all(O.reduce_emulate(S, order=O.TWO_LEVEL, groups=4,
+                                   out_bf16=False) == 5.0)
+
+
+def test_emulate_equals_rounded_reference_on_integers():
+    w = I.with_shape(I.WORKLOADS["llama8b"], M=64, N=128, K=128, W=8)
+    x = I.make_inputs(w, seed=11, dist="ternary")
+    ref = O.reference_rows(x["A"], x["B"], dtype=O.BF16)
+    em = O.emulate_rows(x["A"], x["B"], dtype=O.BF16)
+    assert np.array_equal(em, O.bf16_rne(ref.astype(np.float32)).reshape(em.shape))
+
+
+def test_emulate_close_to_reference_on_floats():
+    w = I.with_shape(I.WORKLOADS["llama8b"], M=32, N=64, K=128)
+    x = I.make_inputs(w, seed=12)
+    ref = O.reference_rows(x["A"], x["B"], dtype=O.BF16)
+    em = O.bf16_bits_to_f64(O.emulate_rows(x["A"], x["B"], dtype=O.BF16))
+    assert O.max_norm_err(em.reshape(ref.shape), ref) < 2**-8
+
+
+# ---------------------------------------------------------- tile map, swizzle
+def _geom_cases():
+    cases = [
+        (I.WORKLOADS["tiny_f32"], 64, 64),
+        (I.WORKLOADS["llama8b"], 256, 256),
+        (I.WORKLOADS["llama70b"], 256, 256),
+        (I.WORKLOADS["decode"], 64, 128),
+        (I.WORKLOADS["ragged_2lvl"], 256, 256),
+    ]
+    return [(w.M, w.N, w.K, w.W, bm, bn) for w, bm, bn in cases]
+
+
+def _random_geoms(n=60):
+    rng = np.random.default_rng(13)
+    out = []
+    for _ in range(n):
+        W = int(rng.integers(1, 9))
+        Mc = int(rng.integers(1, 70))
+        bm = int(rng.choice([8, 16, 32, 64]))
+        bn = int(rng.choice([8, 16]))
+        tn = int(rng.integers(1, 5))
+        out.append((W * Mc, bn * tn, 64, W, bm, bn))
+    return out
+
+
+@pytest.mark.parametrize("swz", [O.REMOTE_FIRST, O.SELF_FIRST, O.IDENTITY])
+@pytest.mark.parametrize("g", [1, 2, 3])
+def test_seq_is_permutation(swz, g):
+    for (M, N, K, W, bm, bn) in _geom_cases() + _random_geoms():
+        G = O.Geometry(M, N, K, W, bm, bn, group_m=g, swizzle=swz)
+        tab = G.seq_table()
+        assert tab.shape == (W, G.T)
+        for r in range(W):
+            assert sorted(tab[r].tolist()) == list(range(G.T))
+            # tiles come chunk by chunk in dest order
+            owners = [G.owner(t // G.tiles_n) for t in tab[r]]
+            steps = {G.dest(r, s): s for s in range(W)}
+            s_of = [steps[d] for d in owners]
+            assert s_of == sorted(s_of)
+        tr = G.trace()
+        assert sorted(tr.tolist()) == sorted(list(range(G.T)) * W)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 16, 64])
+def test_dest_is_latin_square_remote_first(W):
+    G = O.Geometry(W * 4, 64, 64, W, 4, 64)
+    D = np.array([[G.dest(r, s) for s in range(W)] for r in range(W)])
+    for s in range(W):
+        assert sorted(D[:, s]) == list(range(W))   # distinct targets per step
+    for r in range(W):
+        assert sorted(D[r]) == list(range(W))      # every chunk once per rank
+        assert D[r, W - 1] == r                    # local chunk last
+        if W > 1:
+            assert D[r, 0] != r                    # remote chunk first
+
+
+def test_self_first_matches_page_example():
+    rows = {}
+    with open(os.path.join(GOLDEN, "swizzle_rank_offset_w8.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split(":")
+                rows[int(k)] = [int(x) for x in v.split()]
+    G = O.Geometry(8 * 256, 256, 64, 8, 256, 256, swizzle=O.SELF_FIRST)
+    for r, want in rows.items():
+        assert [G.dest(r, s) for s in range(8)] == want
+    # the default order is the same rotation shifted by one step: local last
+    R = O.Geometry(8 * 256, 256, 64, 8, 256, 256, swizzle=O.REMOTE_FIRST)
+    for r, want in rows.items():
+        assert [R.dest(r, s) for s in range(8)] == want[1:] + want[:1]
+
+
+def test_identity_swizzle_same_order_everywhere():
+    G = O.Geometry(8 * 512, 1024, 64, 8, 256, 256, swizzle=O.IDENTITY)
+    tab = G.seq_table()
+    assert all(np.array_equal(tab[0], tab[r]) for r in range(8))
+    assert tab[0].tolist() == list(range(G.T))
+
+
+def test_tiny_worked_example():
+    # W=2, M=128, N=256, 64x64 tiles: tiles_m=2, tiles_n=4, T=8, Mc=64.
+    # tile-row 0 belongs to chunk 0, tile-row 1 to chunk 1.
+    # rank 0: remote chunk 1 first (tiles 4..7), then local chunk 0 (0..3);
+    # rank 1: remote chunk 0 first (0..3), then chunk 1 (4..7).
+    G = O.Geometry(128, 256, 512, 2, 64, 64)
+    assert G.T == 8 and G.Mc == 64
+    assert G.seq(0) == [4, 5, 6, 7, 0, 1, 2, 3]
+    assert G.seq(1) == [0, 1, 2, 3, 4, 5, 6, 7]
+    assert G.trace().tolist() == [4, 0, 5, 1, 6, 2, 7, 3, 0, 4, 1, 5, 2, 6, 3, 7]
+
+
+def test_group_m_order_hand_example():
+    # W=1, 4 tile-rows x 3 tile-columns, groups of 2 tile-rows:
+    # (tm,tn) order (0,0)(1,0)(0,1)(1,1)(0,2)(1,2)(2,0)(3,0)(2,1)(3,1)(2,2)(3,2)
+    G = O.Geometry(4 * 16, 3 * 16, 64, 1, 16, 16, group_m=2)
+    assert G.seq(0) == [0, 3, 1, 4, 2, 5, 6, 9, 7, 10, 8, 11]
+    # a ragged last group (3 tile-rows, g=2): the lone last row goes alone
+    G = O.Geometry(3 * 16, 2 * 16, 64, 1, 16, 16, group_m=2)
+    assert G.seq(0) == [0, 2, 1, 3, 4, 5]
+
+
+def test_ragged_straddle_rows():
+    w = I.WORKLOADS["ragged_2lvl"]
+    G = O.Geometry(w.M, w.N, w.K, w.W, 256, 256)
+    assert G.Mc == 1000 and G.tiles_m == 32
+    assert G.straddling_tile_rows() == [3, 7, 11, 15, 19, 23, 27]
+    assert G.tile_rows(31) == (7936, 8000)
+    assert [G.chunk_of_row(i) for i in (999, 1000, 7999)] == [0, 1, 7]
+
+
+def test_decode_degenerate_order():
+    # M=64 with 64-row tiles: one tile-row, owned by chunk 0; every rank's
+    # order is the same 64 tiles, and chunks 1..7 own no tile-row
+    w = I.WORKLOADS["decode"]
+    G = O.Geometry(w.M, w.N, w.K, w.W, 64, 128)
+    assert G.T == 64 and G.straddling_tile_rows() == [0]
+    for r in range(8):
+        assert G.seq(r) == list(range(64))
+    assert [len(G.chunk_tile_rows(d)) for d in range(8)] == [1] + [0] * 7
+
+
+def test_staging_offsets_are_a_bijection():
+    for (M, N, K, W, bm, bn) in _random_geoms(25):
+        G = O.Geometry(M, N, K, W, bm, bn)
+        seen = np.zeros(W * M * N, dtype=np.int32)
+        # every element of every rank's output, walked tile by tile
+        for r in range(W):
+            for t in range(G.T):
+                tm, tn = divmod(t, G.tiles_n)
+                lo, hi = G.tile_rows(tm)
+                for i in range(lo, hi):
+                    d = G.chunk_of_row(i)
+                    for j in range(tn * bn, (tn + 1) * bn):
+                        seen[G.staging_offset(d, r, i, j)] += 1
+        assert np.all(seen == 1)
+
+
+def test_staging_offset_hand_values():
+    # W=2, M=4 (Mc=2), N=3: S[d][r][il][j]
+    G = O.Geometry(4, 3, 64, 2, 2, 3)
+    assert G.staging_offset(0, 0, 0, 0) == 0
+    assert G.staging_offset(0, 1, 1, 2) == (1 * 2 + 1) * 3 + 2
+    assert G.staging_offset(1, 0, 2, 0) == (2 * 2 + 0) * 3
+    assert G.staging_offset(1, 1, 3, 2) == 4 * 2 * 3 - 1
+
+
+def test_flag_prediction():
+    G = O.Geometry(128, 256, 512, 2, 64, 64)
+    assert not G.predict_flags([3]).any()
+    assert G.predict_flags([1]).all()
+    assert G.predict_flags([3 | O.KEEP_FLAGS]).all()
+    assert not G.predict_flags([1, 2]).any()
+    assert not G.predict_flags([3, 3, 3]).any()
+
+
+# ---------------------------------------------------------------- validate
+TILES = [(256, 256), (64, 64)]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), O.OK),
+    (dict(W=0), O.INVALID_ARG),
+    (dict(W=65), O.INVALID_ARG),
+    (dict(M=1000, W=3), O.INVALID_ARG),
+    (dict(M=0), O.INVALID_ARG),
+    (dict(dtype=7), O.INVALID_ARG),
+    (dict(order=2), O.INVALID_ARG),
+    (dict(order=O.TWO_LEVEL, groups=3), O.INVALID_ARG),
+    (dict(order=O.TWO_LEVEL, groups=0), O.INVALID_ARG),
+    (dict(order=O.TWO_LEVEL, groups=2), O.OK),
+    (dict(swizzle=3), O.INVALID_ARG),
+    (dict(has_c=1, ldc=100), O.INVALID_ARG),
+    (dict(has_c=1, ldc=0), O.OK),
+    (dict(has_c=1, ldc=1024), O.OK),
+    (dict(has_c=1, ldc=1028), O.UNSUPPORTED),
+    (dict(materialize_sub=1), O.INVALID_ARG),
+    (dict(materialize_sub=1, order=O.TWO_LEVEL, groups=2), O.OK),
+    (dict(group_m=-1), O.INVALID_ARG),
+    (dict(tile_m=128, tile_n=128), O.UNSUPPORTED),
+    (dict(N=1000), O.UNSUPPORTED),
+    (dict(K=100), O.UNSUPPORTED),
+])
+def test_validate_table(kw, code):
+    base = dict(M=2048, N=1024, K=512, W=8, dtype=O.BF16, tile_m=256,
+                tile_n=256)
+    base.update(kw)
+    assert O.validate(**base, supported_tiles=TILES) == code
