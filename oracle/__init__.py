@@ -62,7 +62,8 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     UNSUPPORTED: a valid problem outside what the kernels implement: a tile
     shape not in ``supported_tiles``, N not a multiple of the tile width,
     K not a multiple of the 64-deep K step, a C row pitch that is not a
-    multiple of 8 elements (16-byte rows), or a grid too large for 32-bit
+    multiple of 8 elements (16-byte rows), M, N or K of 2^31 or more,
+    or a grid too large for 32-bit
     workgroup ids.
     """
     ints = (M, N, K, W, dtype, tile_m, tile_n, group_m, order, groups,
@@ -95,6 +96,8 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     if N % tile_n != 0 or K % K_STEP != 0:
         return UNSUPPORTED
     if has_c and ldc % 8 != 0:
+        return UNSUPPORTED
+    if max(M, N, K) > 2**31 - 1:
         return UNSUPPORTED
     tiles = -(-M // tile_m) * (N // tile_n)
     if tiles * W > 2**31 - 1:

@@ -1,0 +1,320 @@
+// Host side of the C ABI: descriptor validation, workspace ownership and
+// kernel launch sequencing.  No host synchronisation and no memset on the
+// run path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gemm_rs.h"
+#include "gemm_rs_internal.h"
+
+using namespace gemm_rs;
+
+struct gemm_rs_plan_s {
+    gemm_rs_desc_t d;        // resolved (tiles, group_m, timeout filled in)
+    TileGeom g;
+    int device;
+    int32_t units_per_tile;
+    uint64_t timeout_ticks;
+    float *staging;
+    uint32_t *flags;         // [W][T]
+    uint32_t *counters;      // [T]
+    uint32_t *sub_counters;  // [G][T] (materialised two-level)
+    float *sub;              // [W][G][Mc][N]
+    uint32_t *sub_flags;     // [G][T*units]
+    int32_t *err;            // 4 words
+    int32_t *trace;          // [W*T]
+    int64_t staging_bytes, flags_bytes, counters_bytes, sub_bytes,
+        sub_flags_bytes, trace_bytes;
+};
+
+namespace {
+
+constexpr int kMaxW = 64;
+constexpr int kKStep = 64;
+
+bool f32_tile_supported(int32_t bm, int32_t bn) { return bm == 64 && bn == 64; }
+
+// Default tile: the largest supported tile that the shape fills.
+void pick_default_tile(const gemm_rs_desc_t &d, int32_t *bm, int32_t *bn) {
+    if (d.dtype == GEMM_RS_F32) {
+        *bm = d.tile_m ? d.tile_m : 64;
+        *bn = d.tile_n ? d.tile_n : 64;
+        return;
+    }
+    int32_t m = d.tile_m, n = d.tile_n;
+    if (m == 0) m = (d.M <= 64) ? 64 : 256;
+    if (n == 0) {
+        if (m == 64) n = 128;
+        else n = (d.N % 256 == 0) ? 256 : 128;
+    }
+    *bm = m;
+    *bn = n;
+}
+
+// Problem-level checks: INVALID_ARG.  Implementation limits: UNSUPPORTED.
+int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
+    if (d.W < 1 || d.W > kMaxW || d.M < 1 || d.N < 1 || d.K < 1)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (d.M % d.W != 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (d.dtype != GEMM_RS_BF16 && d.dtype != GEMM_RS_F32)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (d.group_m < 0 || d.tile_m < 0 || d.tile_n < 0)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (d.order != GEMM_RS_ORDER_FLAT && d.order != GEMM_RS_ORDER_TWO_LEVEL)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (d.order == GEMM_RS_ORDER_TWO_LEVEL &&
+        (d.groups < 1 || d.W % d.groups != 0))
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (d.swizzle != GEMM_RS_SWIZZLE_REMOTE_FIRST &&
+        d.swizzle != GEMM_RS_SWIZZLE_SELF_FIRST &&
+        d.swizzle != GEMM_RS_SWIZZLE_IDENTITY)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if ((d.has_c != 0 && d.has_c != 1) || d.ldc < 0 ||
+        (d.has_c && d.ldc != 0 && d.ldc < d.N))
+        return GEMM_RS_ERR_INVALID_ARG;
+    if ((d.materialize_sub != 0 && d.materialize_sub != 1) ||
+        (d.materialize_sub && d.order != GEMM_RS_ORDER_TWO_LEVEL))
+        return GEMM_RS_ERR_INVALID_ARG;
+    bool tile_ok = d.dtype == GEMM_RS_BF16 ? bf16_tile_supported(bm, bn)
+                                           : f32_tile_supported(bm, bn);
+    if (!tile_ok) return GEMM_RS_ERR_UNSUPPORTED;
+    if (d.N % bn != 0 || d.K % kKStep != 0) return GEMM_RS_ERR_UNSUPPORTED;
+    if (d.has_c && d.ldc % 8 != 0) return GEMM_RS_ERR_UNSUPPORTED;
+    if (d.M > INT32_MAX || d.N > INT32_MAX || d.K > INT32_MAX)
+        return GEMM_RS_ERR_UNSUPPORTED;
+    int64_t tiles = ((d.M + bm - 1) / bm) * (d.N / bn);
+    if (tiles * d.W > INT32_MAX) return GEMM_RS_ERR_UNSUPPORTED;
+    // staging W*M*N floats must be addressable with 64-bit offsets
+    if ((double)d.W * (double)d.M * (double)d.N * 4.0 > 9.0e18)
+        return GEMM_RS_ERR_UNSUPPORTED;
+    return GEMM_RS_OK;
+}
+
+void free_plan(gemm_rs_plan_s *p) {
+    if (!p) return;
+    int cur = -1;
+    bool switched = false;
+    if (hipGetDevice(&cur) == hipSuccess && cur != p->device)
+        switched = hipSetDevice(p->device) == hipSuccess;
+    hipFree(p->staging);
+    hipFree(p->flags);
+    hipFree(p->counters);
+    hipFree(p->sub_counters);
+    hipFree(p->sub);
+    hipFree(p->sub_flags);
+    hipFree(p->err);
+    hipFree(p->trace);
+    if (switched) hipSetDevice(cur);
+    free(p);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Zero every flag, counter and the error word (plan time and after errors).
+hipError_t clear_protocol_state(gemm_rs_plan_s *p, hipStream_t s) {
+    hipError_t e = hipMemsetAsync(p->flags, 0, p->flags_bytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p->counters, 0, p->counters_bytes, s);
+    if (e == hipSuccess && p->sub_counters)
+        e = hipMemsetAsync(p->sub_counters, 0, p->counters_bytes * p->d.groups, s);
+    if (e == hipSuccess && p->sub_flags)
+        e = hipMemsetAsync(p->sub_flags, 0, p->sub_flags_bytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p->err, 0, 4 * sizeof(int32_t), s);
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_rs_strerror(int code) {
+    switch (code) {
+    case GEMM_RS_OK: return "ok";
+    case GEMM_RS_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_RS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GEMM_RS_ERR_HIP: return "HIP runtime error";
+    case GEMM_RS_ERR_TIMEOUT: return "device flag wait timed out";
+    case GEMM_RS_ERR_PROTOCOL: return "flag protocol violation";
+    default: return "unknown status";
+    }
+}
+
+int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
+    if (out) *out = nullptr;
+    if (!desc || !out) return GEMM_RS_ERR_INVALID_ARG;
+    gemm_rs_desc_t d = *desc;
+    int32_t bm = 0, bn = 0;
+    pick_default_tile(d, &bm, &bn);
+    int rc = validate(d, bm, bn);
+    if (rc != GEMM_RS_OK) return rc;
+    d.tile_m = bm;
+    d.tile_n = bn;
+    if (d.group_m == 0) d.group_m = 1;
+    if (d.order == GEMM_RS_ORDER_FLAT) d.groups = 1;
+    if (d.timeout_ms == 0) d.timeout_ms = 1000;
+
+    gemm_rs_plan_s *p = (gemm_rs_plan_s *)calloc(1, sizeof(gemm_rs_plan_s));
+    if (!p) return GEMM_RS_ERR_HIP;
+    p->d = d;
+    TileGeom &g = p->g;
+    g.M = d.M; g.N = d.N; g.K = d.K; g.W = d.W; g.Mc = d.M / d.W;
+    g.BM = bm; g.BN = bn;
+    g.tiles_m = (int32_t)((d.M + bm - 1) / bm);
+    g.tiles_n = (int32_t)(d.N / bn);
+    g.T = g.tiles_m * g.tiles_n;
+    g.group_m = d.group_m;
+    g.swizzle = d.swizzle;
+    p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;
+
+    if (hipGetDevice(&p->device) != hipSuccess) { free(p); return GEMM_RS_ERR_HIP; }
+    int rate_khz = 0;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate,
+                              p->device) != hipSuccess || rate_khz <= 0)
+        rate_khz = 100000;  // the 100 MHz constant clock
+    p->timeout_ticks = (uint64_t)d.timeout_ms * (uint64_t)rate_khz;
+
+    p->staging_bytes = (int64_t)d.W * d.M * d.N * 4;
+    p->flags_bytes = (int64_t)d.W * g.T * 4;
+    p->counters_bytes = (int64_t)g.T * 4;
+    p->trace_bytes = (int64_t)d.W * g.T * 4;
+    hipError_t e = hipMalloc(&p->staging, p->staging_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->flags, p->flags_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->counters, p->counters_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->err, 4 * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&p->trace, p->trace_bytes);
+    if (e == hipSuccess && d.materialize_sub) {
+        p->sub_bytes = (int64_t)d.groups * d.M * d.N * 4;
+        p->sub_flags_bytes = (int64_t)d.groups * g.T * p->units_per_tile * 4;
+        e = hipMalloc(&p->sub, p->sub_bytes);
+        if (e == hipSuccess) e = hipMalloc(&p->sub_flags, p->sub_flags_bytes);
+        if (e == hipSuccess)
+            e = hipMalloc(&p->sub_counters, p->counters_bytes * d.groups);
+    }
+    // flags are zeroed once, here; runs keep them at 0 between passes
+    if (e == hipSuccess) e = clear_protocol_state(p, nullptr);
+    if (e == hipSuccess) e = hipMemset(p->trace, 0xff, p->trace_bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_plan(p);
+        return GEMM_RS_ERR_HIP;
+    }
+    *out = p;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_destroy(gemm_rs_plan_t p) {
+    free_plan(p);
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_query(gemm_rs_plan_t p, gemm_rs_info_t *info) {
+    if (!p || !info) return GEMM_RS_ERR_INVALID_ARG;
+    memset(info, 0, sizeof(*info));
+    info->Mc = p->g.Mc;
+    info->tile_m = p->g.BM;
+    info->tile_n = p->g.BN;
+    info->tiles_m = p->g.tiles_m;
+    info->tiles_n = p->g.tiles_n;
+    info->T = p->g.T;
+    info->group_m = p->g.group_m;
+    info->staging = p->staging;
+    info->flags = p->flags;
+    info->sub = p->sub;
+    info->sub_flags = p->sub_flags;
+    info->trace = p->trace;
+    info->staging_bytes = p->staging_bytes;
+    info->flags_bytes = p->flags_bytes;
+    info->sub_bytes = p->sub_bytes;
+    info->sub_flags_bytes = p->sub_flags_bytes;
+    info->workspace_bytes = p->staging_bytes + p->flags_bytes +
+                            p->counters_bytes * (1 + (p->sub_counters ? p->d.groups : 0)) +
+                            p->sub_bytes + p->sub_flags_bytes + p->trace_bytes + 16;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
+                float alpha, float beta, void *out, void *stream,
+                uint32_t run_flags) {
+    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    const uint32_t known = GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE |
+                           GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES;
+    if (run_flags & ~known) return GEMM_RS_ERR_INVALID_ARG;
+    const bool do_gemm = run_flags & GEMM_RS_RUN_GEMM;
+    const bool do_reduce = run_flags & GEMM_RS_RUN_REDUCE;
+    if (do_gemm) {
+        if (!A || !B || !aligned16(A) || !aligned16(B))
+            return GEMM_RS_ERR_INVALID_ARG;
+        if (p->d.has_c && (!C || !aligned16(C))) return GEMM_RS_ERR_INVALID_ARG;
+        if (!p->d.has_c && C) return GEMM_RS_ERR_INVALID_ARG;
+    }
+    if (do_reduce && (!out || !aligned16(out))) return GEMM_RS_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (do_gemm) {
+        GemmArgs a;
+        a.g = p->g;
+        a.A = A; a.B = B; a.C = C;
+        a.ldc = p->d.ldc;
+        a.has_c = p->d.has_c;
+        a.alpha = alpha; a.beta = beta;
+        a.staging = p->staging;
+        a.flags = p->flags;
+        a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
+        hipError_t e = p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(a, s)
+                                                  : launch_gemm_f32(a, s);
+        if (e != hipSuccess) return GEMM_RS_ERR_HIP;
+    }
+    if (do_reduce) {
+        ReduceArgs r;
+        r.g = p->g;
+        r.order = p->d.order;
+        r.groups = p->d.groups;
+        r.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
+        r.units_per_tile = p->units_per_tile;
+        r.timeout_ticks = p->timeout_ticks;
+        r.staging = p->staging;
+        r.out = out;
+        r.flags = p->flags;
+        r.counters = p->counters;
+        r.err = p->err;
+        r.sub = p->sub;
+        r.sub_flags = p->sub_flags;
+        hipError_t e;
+        if (p->d.materialize_sub) {
+            ReduceArgs rs = r;
+            rs.counters = p->sub_counters;
+            e = launch_reduce_sub(rs, s);
+            if (e == hipSuccess) e = launch_reduce_final_sub(r, p->d.dtype, s);
+        } else {
+            e = launch_reduce(r, p->d.dtype, s);
+        }
+        if (e != hipSuccess) return GEMM_RS_ERR_HIP;
+    }
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {
+    if (!p || !host_trace) return GEMM_RS_ERR_INVALID_ARG;
+    hipError_t e = launch_tile_order(p->g, p->trace, nullptr);
+    if (e == hipSuccess)
+        e = hipMemcpy(host_trace, p->trace, p->trace_bytes, hipMemcpyDeviceToHost);
+    return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
+}
+
+int gemm_rs_status(gemm_rs_plan_t p, void *stream, int32_t *detail) {
+    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t e4[4] = {0, 0, 0, 0};
+    if (hipStreamSynchronize(s) != hipSuccess) return GEMM_RS_ERR_HIP;
+    if (hipMemcpy(e4, p->err, sizeof e4, hipMemcpyDeviceToHost) != hipSuccess)
+        return GEMM_RS_ERR_HIP;
+    if (detail) memcpy(detail, e4, sizeof e4);
+    if (e4[0] != 0) {
+        if (clear_protocol_state(p, s) != hipSuccess) return GEMM_RS_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return GEMM_RS_ERR_HIP;
+    }
+    return e4[0];
+}
+
+}  // extern "C"

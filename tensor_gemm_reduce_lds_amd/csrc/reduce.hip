@@ -1,0 +1,293 @@
+// Flag-gated, fixed-order W-way reduction of the staging slots.
+//
+// Work unit: up to kReduceRows rows of one tile.  A unit first waits until
+// every rank's flag for its tile reads 1 (agent-scope acquire, bounded by a
+// timeout on the constant-rate device clock), then sums the W fp32 slots of
+// each element in a fixed order and writes the rank's chunk rows of `out`.
+// The last unit of a tile to pass the wait puts the tile's flags back to 0,
+// so no buffer is ever cleared between runs (page "flux实现：sm80 gemm+rs",
+// section "cutlass自定义epilogue–sm80": the consumer waits on the
+// producer's per-tile flag; section "自己的类flux实现": the pre-clear of
+// the reduce buffer and the syncs around it are the cost being removed).
+//
+// Orders: flat y = ((S_0 + S_1) + ...) + S_{W-1}; two-level with G groups
+// of L = W/G contiguous ranks: each group summed in ascending rank, then
+// the group sums in ascending group (page "flux实现：sm80 gemm+rs", section
+// "2D Ring优化": partial sums inside a level first, then across levels).
+#include "gemm_rs_internal.h"
+
+namespace gemm_rs {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ void record_error(int32_t *err, int code, int32_t r, int32_t t, uint32_t v) {
+    if (atomicCAS(&err[0], 0, code) == 0) {
+        __hip_atomic_store(&err[1], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&err[2], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&err[3], (int32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Wait until *f == 1.  Returns 0, or the error code after recording it.
+__device__ int wait_ready(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
+                          int32_t r, int32_t t) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        const uint32_t v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        if (v == 1u) return 0;
+        if (v != 0u) {
+            record_error(err, GEMM_RS_ERR_PROTOCOL, r, t, v);
+            return GEMM_RS_ERR_PROTOCOL;
+        }
+        if (wall_clock64() - t0 > timeout_ticks) {
+            record_error(err, GEMM_RS_ERR_TIMEOUT, r, t, 0);
+            return GEMM_RS_ERR_TIMEOUT;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Threads [first, first+count) each wait on one flag; true if all ready.
+// Ends with a barrier and an agent-scope acquire fence in every thread, so
+// loads issued afterwards see what the producers stored before releasing.
+__device__ bool wait_flags(uint32_t *base, int64_t stride,
+                           int count, uint64_t timeout_ticks, int32_t *err,
+                           int32_t rank0, int32_t tile) {
+    __shared__ int failed;
+    if (threadIdx.x == 0) failed = 0;
+    __syncthreads();
+    const int i = threadIdx.x;
+    if (i < count) {
+        if (wait_ready(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile))
+            atomicOr(&failed, 1);
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return failed == 0;
+}
+
+__device__ __forceinline__ void store_out4(void *out, int64_t idx, f32x4_t y, bool bf16) {
+    if (bf16) {
+        // fptrunc to bfloat16 rounds to nearest even (v_cvt_pk_bf16_f32)
+        __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1], h2 = (__bf16)y[2], h3 = (__bf16)y[3];
+        uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        u32x2_t w = {w0, w1};
+        *(u32x2_t *)((uint16_t *)out + idx) = w;
+    } else {
+        *(f32x4_t *)((float *)out + idx) = y;
+    }
+}
+
+// Row range of unit `slab` of tile-row tm.
+__device__ __forceinline__ void unit_rows(const TileGeom &g, int32_t tm, int32_t slab,
+                                          int64_t *lo, int64_t *hi) {
+    const int64_t tile_lo = (int64_t)tm * g.BM;
+    int64_t tile_hi = tile_lo + g.BM;
+    if (tile_hi > g.M) tile_hi = g.M;
+    *lo = tile_lo + (int64_t)slab * kReduceRows;
+    *hi = *lo + kReduceRows < tile_hi ? *lo + kReduceRows : tile_hi;
+}
+
+// Sum of one element group (4 columns) over the W slots in the fixed order.
+// `S` points at slot (d, 0) of the element; slots are `stride` floats apart.
+template <int WT>
+__device__ __forceinline__ f32x4_t ordered_sum(const float *S, int64_t stride, int W, int L) {
+    if constexpr (WT > 0) {
+        f32x4_t v[WT];
+#pragma unroll
+        for (int q = 0; q < WT; ++q)
+            v[q] = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
+        f32x4_t y = v[0], s = v[0];
+#pragma unroll
+        for (int q = 0; q < WT; ++q) {
+            s = (q % L == 0) ? v[q] : s + v[q];
+            if (q % L == L - 1) y = (q / L == 0) ? s : y + s;
+        }
+        return y;
+    } else {
+        f32x4_t y = {0, 0, 0, 0}, s = {0, 0, 0, 0};
+        for (int q = 0; q < W; ++q) {
+            f32x4_t v = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
+            s = (q % L == 0) ? v : s + v;
+            if (q % L == L - 1) y = (q / L == 0) ? s : y + s;
+        }
+        return y;
+    }
+}
+
+// One-stage reduce: flags -> out.
+template <int WT, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
+    const TileGeom &g = a.g;
+    const int32_t U = a.units_per_tile;
+    const int32_t t = (int32_t)(blockIdx.x / U), slab = (int32_t)(blockIdx.x % U);
+    const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
+
+    if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t)) return;
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(&a.counters[t], 1u);
+        if (old == (uint32_t)U - 1) {   // every unit of the tile has passed
+            if (!a.keep_flags)
+                for (int q = 0; q < g.W; ++q)
+                    __hip_atomic_store(&a.flags[(int64_t)q * g.T + t], 0u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    int64_t lo, hi;
+    unit_rows(g, tm, slab, &lo, &hi);
+    const int W = g.W, L = W / a.groups;
+    const int C4 = g.BN / 4;
+    const int64_t n4 = (hi - lo) * C4;
+    const int64_t stride = g.Mc * g.N;
+    for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
+        const int64_t row = lo + e / C4;
+        const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
+        const int64_t d = row / g.Mc;
+        const float *S = a.staging + ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
+        const f32x4_t y = ordered_sum<WT>(S, stride, W, L);
+        store_out4(a.out, row * g.N + col, y, OUT_BF16);
+    }
+}
+
+// Materialised two-level, stage 1: group g's partial sum -> sub buffer.
+template <int LT>
+__global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
+    const TileGeom &g = a.g;
+    const int32_t U = a.units_per_tile, G = a.groups, L = g.W / G;
+    const int64_t per_group = (int64_t)g.T * U;
+    const int32_t grp = (int32_t)(blockIdx.x / per_group);
+    const int64_t unit = blockIdx.x - (int64_t)grp * per_group;
+    const int32_t t = (int32_t)(unit / U), slab = (int32_t)(unit % U);
+    const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
+
+    if (!wait_flags(a.flags + (int64_t)grp * L * g.T + t, g.T, L,
+                    a.timeout_ticks, a.err, grp * L, t))
+        return;
+    if (threadIdx.x == 0) {
+        uint32_t *cnt = &a.counters[(int64_t)grp * g.T + t];
+        const uint32_t old = atomicAdd(cnt, 1u);
+        if (old == (uint32_t)U - 1) {
+            if (!a.keep_flags)
+                for (int q = 0; q < L; ++q)
+                    __hip_atomic_store(&a.flags[(int64_t)(grp * L + q) * g.T + t], 0u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    int64_t lo, hi;
+    unit_rows(g, tm, slab, &lo, &hi);
+    const int C4 = g.BN / 4;
+    const int64_t n4 = (hi - lo) * C4;
+    const int64_t stride = g.Mc * g.N;
+    for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
+        const int64_t row = lo + e / C4;
+        const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
+        const int64_t d = row / g.Mc, il = row - d * g.Mc;
+        const float *S = a.staging + ((d * g.W + (int64_t)grp * L) * g.Mc + il) * g.N + col;
+        const f32x4_t s = ordered_sum<LT>(S, stride, L, L);
+        float *dst = a.sub + ((d * G + grp) * g.Mc + il) * g.N + col;
+        __builtin_nontemporal_store(s, (f32x4_t *)dst);
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.sub_flags[(int64_t)grp * per_group + unit], 1u,
+                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Materialised two-level, stage 2: y = ((S_0 + S_1) + ...) -> out.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a) {
+    const TileGeom &g = a.g;
+    const int32_t U = a.units_per_tile, G = a.groups;
+    const int64_t per_group = (int64_t)g.T * U;
+    const int64_t unit = blockIdx.x;
+    const int32_t t = (int32_t)(unit / U), slab = (int32_t)(unit % U);
+    const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
+
+    if (!wait_flags(a.sub_flags + unit, per_group, G, a.timeout_ticks,
+                    a.err, 0, t))
+        return;
+    // a sub-flag has exactly one consumer: reset it right after the wait
+    if (threadIdx.x < G && !a.keep_flags)
+        __hip_atomic_store(&a.sub_flags[(int64_t)threadIdx.x * per_group + unit], 0u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    int64_t lo, hi;
+    unit_rows(g, tm, slab, &lo, &hi);
+    const int C4 = g.BN / 4;
+    const int64_t n4 = (hi - lo) * C4;
+    const int64_t stride = g.Mc * g.N;
+    for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
+        const int64_t row = lo + e / C4;
+        const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
+        const int64_t d = row / g.Mc, il = row - d * g.Mc;
+        const float *S = a.sub + ((d * G) * g.Mc + il) * g.N + col;
+        const f32x4_t y = ordered_sum<0>(S, stride, G, G);
+        store_out4(a.out, row * g.N + col, y, OUT_BF16);
+    }
+}
+
+__global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= (int64_t)g.W * g.T) return;
+    int32_t r, t;
+    tile_of_block(g, b, &r, &t);
+    trace[b] = t;
+}
+
+template <bool BF>
+hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.g.T * a.units_per_tile));
+    switch (a.g.W) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<0, BF>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceArgs &a, int dtype, hipStream_t s) {
+    return dtype == GEMM_RS_BF16 ? launch_flat<true>(a, s) : launch_flat<false>(a, s);
+}
+
+hipError_t launch_reduce_sub(const ReduceArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.groups * a.g.T * a.units_per_tile));
+    const int L = a.g.W / a.groups;
+    switch (L) {
+    case 4: hipLaunchKernelGGL((reduce_sub_kernel<4>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((reduce_sub_kernel<0>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_final_sub(const ReduceArgs &a, int dtype, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.g.T * a.units_per_tile));
+    if (dtype == GEMM_RS_BF16)
+        hipLaunchKernelGGL((reduce_final_sub_kernel<true>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((reduce_final_sub_kernel<false>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_order(const TileGeom &g, int32_t *trace, hipStream_t s) {
+    const int64_t n = (int64_t)g.W * g.T;
+    hipLaunchKernelGGL(tile_order_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       g, trace);
+    return hipGetLastError();
+}
+
+}  // namespace gemm_rs

@@ -1,0 +1,90 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad descriptors before any HIP call with
+the same status the oracle's rules give."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle as O
+from tensor_gemm_reduce_lds_amd import gemm_rs as G
+
+BF16_TILES = [(256, 256), (256, 128), (128, 128), (64, 128)]
+F32_TILES = [(64, 64)]
+
+
+def test_library_exports_every_header_function():
+    names = G.header_functions()
+    assert names == sorted(["gemm_rs_plan", "gemm_rs_run", "gemm_rs_destroy",
+                            "gemm_rs_query", "gemm_rs_tile_order",
+                            "gemm_rs_status", "gemm_rs_strerror"])
+    lib = G.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _c_layout(tmp_path):
+    """sizeof/offsetof of the public structs as gcc lays them out."""
+    fields_d = [f[0] for f in G.gemm_rs_desc_t._fields_]
+    fields_i = [f[0] for f in G.gemm_rs_info_t._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "gemm_rs.h"',
+           "int main(void) {",
+           '  printf("desc %zu\\n", sizeof(gemm_rs_desc_t));',
+           '  printf("info %zu\\n", sizeof(gemm_rs_info_t));']
+    for f in fields_d:
+        src.append('  printf("d.%s %%zu\\n", offsetof(gemm_rs_desc_t, %s));' % (f, f))
+    for f in fields_i:
+        src.append('  printf("i.%s %%zu\\n", offsetof(gemm_rs_info_t, %s));' % (f, f))
+    src.append("  return 0; }")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(G.HEADER), str(c), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return dict(line.split() for line in out.splitlines())
+
+
+def test_struct_layout_matches_c_compiler(tmp_path):
+    lay = _c_layout(tmp_path)
+    assert int(lay["desc"]) == ctypes.sizeof(G.gemm_rs_desc_t)
+    assert int(lay["info"]) == ctypes.sizeof(G.gemm_rs_info_t)
+    for f, _ in G.gemm_rs_desc_t._fields_:
+        assert int(lay["d." + f]) == getattr(G.gemm_rs_desc_t, f).offset, f
+    for f, _ in G.gemm_rs_info_t._fields_:
+        assert int(lay["i." + f]) == getattr(G.gemm_rs_info_t, f).offset, f
+
+
+def test_strerror_and_null_handles():
+    assert G.gemm_rs_strerror(0) == "ok"
+    assert "timed out" in G.gemm_rs_strerror(G.ERR_TIMEOUT)
+    assert G.gemm_rs_strerror(12345) == "unknown status"
+    rc, h = G.gemm_rs_plan(None)
+    assert rc == G.ERR_INVALID_ARG and h is None
+    assert G.gemm_rs_run(None, None, None, None, 1.0, 0.0, None) == G.ERR_INVALID_ARG
+    assert G.gemm_rs_destroy(None) == G.OK
+    assert G.gemm_rs_query(None)[0] == G.ERR_INVALID_ARG
+    assert G.gemm_rs_status(None)[0] == G.ERR_INVALID_ARG
+
+
+BAD = [
+    dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=0), dict(dtype=7),
+    dict(order=2), dict(order=1, groups=3), dict(order=1, groups=0), dict(swizzle=3),
+    dict(has_c=1, ldc=100), dict(has_c=2), dict(ldc=-8), dict(materialize_sub=1),
+    dict(materialize_sub=2, order=1, groups=2), dict(group_m=-1), dict(tile_m=-64),
+    dict(tile_m=128, tile_n=64), dict(tile_m=32, tile_n=32), dict(N=1000),
+    dict(K=100), dict(has_c=1, ldc=1028), dict(dtype=1, tile_m=128, tile_n=128),
+    dict(M=2**31, W=1), dict(K=2**31 + 64),
+]
+
+
+@pytest.mark.parametrize("kw", BAD)
+def test_bad_descriptors_rejected_like_oracle(kw):
+    base = dict(M=2048, N=1024, K=512, W=8, dtype=0, tile_m=256, tile_n=256)
+    base.update(kw)
+    tiles = F32_TILES if base["dtype"] == 1 else BF16_TILES
+    want = O.validate(**base, supported_tiles=tiles)
+    assert want != O.OK
+    rc, h = G.gemm_rs_plan(G.make_desc(**base))
+    assert rc == want and h is None

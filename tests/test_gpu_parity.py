@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases compare every output element; the five workloads at full size
+are checked on sampled rows and elements the oracle computes one by one,
+plus properties that hold at any size (integer-valued exactness of every
+staging slot, alpha scaling, poison-filled staging)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from tensor_gemm_reduce_lds_amd import gemm_rs as G
+from tensor_gemm_reduce_lds_amd import inputs as I
+
+from gpu_util import (check_tolerance, d2h, desc_fields, flags, geometry, h2d,
+                      new_out, oracle_kw, out_bits, out_to_f64, run_checked, say,
+                      staging_rows, sync, to_device)
+
+pytestmark = pytest.mark.gpu
+
+W70 = I.WORKLOADS
+
+# (name, workload) small enough for a full oracle comparison; they span
+# several tiles, ragged last tile-rows and tiles that straddle chunks.
+SMALL = [
+    ("tiny_f32", W70["tiny_f32"]),
+    ("bf16_256x256_ragged", I.with_shape(W70["llama8b"], W=8, M=800, N=512, K=256,
+                                         tile_m=256, tile_n=256)),
+    ("bf16_256x128_w4", I.with_shape(W70["llama8b"], W=4, M=520, N=384, K=192,
+                                     tile_m=256, tile_n=128)),
+    ("bf16_128x128_fullc", I.with_shape(W70["llama70b"], W=8, M=320, N=256, K=320,
+                                        tile_m=128, tile_n=128, ldc=256,
+                                        alpha=1.25, beta=0.75, c_std=1.0)),
+    ("bf16_64x128_bias", I.with_shape(W70["llama70b"], W=8, M=64, N=1024, K=512,
+                                      tile_m=64, tile_n=128)),
+    ("bf16_two_level", I.with_shape(W70["ragged_2lvl"], M=560, N=512, K=128,
+                                    tile_m=256, tile_n=256)),
+    ("bf16_w1", I.with_shape(W70["llama8b"], W=1, M=256, N=256, K=64,
+                             tile_m=256, tile_n=256)),
+    ("bf16_mc1", I.with_shape(W70["llama8b"], W=8, M=8, N=128, K=64,
+                              tile_m=64, tile_n=128)),
+]
+
+
+def _run_small(w, seed=0, **over):
+    x = I.make_inputs(w, seed=seed)
+    say("case", w.name, w.W, w.M, w.N, w.K, over)
+    dev = to_device(x, w)
+    with G.Plan(**desc_fields(w, **over)) as plan:
+        out = new_out(w)
+        run_checked(plan, dev, w, out)
+        got = out_to_f64(out, w)
+        assert not flags(plan).any()
+        bits = out_bits(out)
+    ref = O.reference_rows(x["A"], x["B"], x["C"], **oracle_kw(w))
+    return got, ref, bits
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[s[0] for s in SMALL])
+def test_small_full_parity(name, w):
+    got, ref, _ = _run_small(w)
+    mx, rf = check_tolerance(got, ref, w.dtype)
+    say("  max_norm_err %.3e rel_F %.3e" % (mx, rf))
+
+
+def test_materialised_two_level_matches_register_two_level():
+    w = dict(SMALL)["bf16_two_level"]
+    _, ref, bits_reg = _run_small(w)
+    got, _, bits_mat = _run_small(w, materialize_sub=1)
+    check_tolerance(got, ref, w.dtype)
+    assert np.array_equal(bits_reg, bits_mat)
+
+
+@pytest.mark.parametrize("over", [dict(swizzle=G.SWIZZLE_SELF_FIRST),
+                                  dict(swizzle=G.SWIZZLE_IDENTITY),
+                                  dict(group_m=2), dict(group_m=3)])
+def test_tile_order_does_not_change_bits(over):
+    w = dict(SMALL)["bf16_256x256_ragged"]
+    _, _, base = _run_small(w)
+    _, _, other = _run_small(w, **over)
+    assert np.array_equal(base, other)
+
+
+# ---------------------------------------------------------------- tile order
+ORDER_CASES = [
+    ("tiny_f32", {}), ("llama8b", {}), ("llama70b", {}), ("decode", {}),
+    ("ragged_2lvl", {}), ("llama70b", dict(group_m=4)),
+    ("ragged_2lvl", dict(group_m=3)), ("llama8b", dict(swizzle=G.SWIZZLE_SELF_FIRST)),
+    ("llama8b", dict(swizzle=G.SWIZZLE_IDENTITY)),
+]
+
+
+@pytest.mark.parametrize("name,over", ORDER_CASES)
+def test_tile_order_matches_oracle_bit_exact(name, over):
+    w = W70[name]
+    say("tile order", name, over)
+    with G.Plan(**desc_fields(w, **over)) as plan:
+        got = plan.tile_order()
+        want = geometry(w, plan).trace()
+    assert np.array_equal(got, want)
+
+
+def test_gemm_trace_matches_oracle():
+    w = dict(SMALL)["bf16_256x256_ragged"]
+    x = I.make_inputs(w)
+    dev = to_device(x, w)
+    say("gemm trace", w.name)
+    with G.Plan(**desc_fields(w, group_m=2)) as plan:
+        out = new_out(w)
+        run_checked(plan, dev, w, out, G.RUN_ALL | G.TRACE_TILES)
+        tr = d2h(plan.info.trace, w.W * plan.info.T * 4, np.int32)
+        assert np.array_equal(tr, geometry(w, plan).trace())
+
+
+# -------------------------------------------------------- full-size workloads
+FULL = ["llama8b", "llama70b", "decode", "ragged_2lvl"]
+
+
+def _sample_rows(w, rng, per_chunk=2):
+    Mc = w.M // w.W
+    rows = set()
+    for d in range(w.W):
+        rows.add(d * Mc)
+        rows.add(d * Mc + Mc - 1)
+        for _ in range(per_chunk - 2):
+            rows.add(d * Mc + int(rng.integers(0, Mc)))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    w = W70[name]
+    rng = np.random.default_rng(100)
+    x = I.make_inputs(w)
+    say("full", name)
+    dev = to_device(x, w)
+    with G.Plan(**desc_fields(w)) as plan:
+        out = new_out(w)
+        run_checked(plan, dev, w, out)
+        got = out_to_f64(out, w)
+        assert not flags(plan).any()
+    del dev
+    kw = oracle_kw(w)
+    rows = _sample_rows(w, rng)
+    ref_rows = np.concatenate([O.reference_rows(x["A"], x["B"], x["C"], row_lo=i,
+                                                row_hi=i + 1, **kw) for i in rows])
+    check_tolerance(got[rows], ref_rows, w.dtype)
+    ii = rng.integers(0, w.M, size=3000)
+    jj = rng.integers(0, w.N, size=3000)
+    ref_e = O.reference_elems(x["A"], x["B"], x["C"], ii=ii, jj=jj, **kw)
+    mx, rf = check_tolerance(got[ii, jj], ref_e, w.dtype)
+    say("  sampled max_norm_err %.3e rel_F %.3e" % (mx, rf))
+    assert np.isfinite(got).all()
+
+
+def test_alpha_half_is_exact_half():
+    # power-of-two scaling commutes with fp32 adds and bf16 rounding, so a
+    # deterministic kernel gives exactly half the alpha=1 output
+    w = W70["ragged_2lvl"]
+    x = I.make_inputs(w)
+    dev = to_device(x, w)
+    say("alpha half", w.name)
+    with G.Plan(**desc_fields(w)) as plan:
+        o1, oh = new_out(w), new_out(w)
+        run_checked(plan, dev, w, o1, alpha=1.0)
+        run_checked(plan, dev, w, oh, alpha=0.5)
+        a1, ah = out_to_f64(o1, w), out_to_f64(oh, w)
+    assert np.array_equal(ah, 0.5 * a1)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_integer_inputs_bit_exact_everywhere(name):
+    """Entries in {-1,0,1}: every partial is a small integer, exact in the
+    fp32 MFMA accumulators and staging, so staging slots must equal the
+    oracle's partials bit for bit and the output must equal emulate mode.
+    Staging is filled with NaN first: any element the GEMM fails to write
+    shows up."""
+    w = W70[name]
+    x = I.make_inputs(w, dist="ternary", c_dist="ternary")
+    rng = np.random.default_rng(7)
+    dev = to_device(x, w)
+    say("integer exactness", name)
+    kw = oracle_kw(w)
+    with G.Plan(**desc_fields(w)) as plan:
+        geom = geometry(w, plan)
+        ptr, nbytes = plan.info.staging, plan.info.staging_bytes
+        import ctypes
+        from gpu_util import hip
+        hip().hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+        assert hip().hipMemset(ptr, 0xFF, nbytes) == 0
+        out = new_out(w)
+        run_checked(plan, dev, w, out, G.RUN_GEMM)
+        assert flags(plan).all()
+        st = d2h(ptr, nbytes, np.float32)
+        assert not np.isnan(st).any(), "staging elements left unwritten"
+        del st
+        rows = _sample_rows(w, rng, per_chunk=3)
+        for i in rows:
+            d = i // geom.Mc
+            for r in range(w.W):
+                want = O.partial_rows(x["A"], x["B"], x["C"], dtype=kw["dtype"],
+                                      alpha=w.alpha, beta=w.beta, ldc=w.ldc, r=r,
+                                      row_lo=i, row_hi=i + 1)[0].astype(np.float32)
+                got = staging_rows(plan, geom, d, r, i - d * geom.Mc, 1)[0]
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (i, r)
+        run_checked(plan, dev, w, out, G.RUN_REDUCE)
+        assert not flags(plan).any()
+        bits = out_bits(out)
+    for i in rows:
+        em = O.emulate_rows(x["A"], x["B"], x["C"], row_lo=i, row_hi=i + 1, **kw)
+        assert np.array_equal(bits[i], em[0].view(bits.dtype)), i

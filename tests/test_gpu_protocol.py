@@ -1,0 +1,160 @@
+"""GPU protocol tests: flag life cycle, split runs, back-to-back runs with no
+host sync, timeouts and stale flags forced from the host (every kernel
+still exits: waits are bounded), and the reduce order checked bit for bit
+on staging contents written by the test."""
+import numpy as np
+import pytest
+
+import oracle as O
+from tensor_gemm_reduce_lds_amd import gemm_rs as G
+from tensor_gemm_reduce_lds_amd import inputs as I
+
+from gpu_util import (desc_fields, flags, h2d, new_out, out_bits, run_checked,
+                      say, sync, to_device)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = I.with_shape(I.WORKLOADS["llama70b"], W=8, M=800, N=512, K=128,
+                     tile_m=256, tile_n=256)
+
+
+def _setup(w=SMALL, **over):
+    x = I.make_inputs(w)
+    return x, to_device(x, w), G.Plan(**desc_fields(w, **over))
+
+
+def test_flag_life_cycle_and_split_runs():
+    say("flag life cycle")
+    x, dev, plan = _setup()
+    with plan:
+        ref = new_out(SMALL)
+        run_checked(plan, dev, SMALL, ref)
+        assert not flags(plan).any()
+        o = new_out(SMALL)
+        run_checked(plan, dev, SMALL, o, G.RUN_ALL | G.KEEP_FLAGS)
+        assert flags(plan).all()
+        run_checked(plan, dev, SMALL, o)            # GEMM re-sets 1s, reduce clears
+        assert not flags(plan).any()
+        run_checked(plan, dev, SMALL, o, G.RUN_GEMM)
+        assert flags(plan).all()
+        o2 = new_out(SMALL)
+        run_checked(plan, dev, SMALL, o2, G.RUN_REDUCE)
+        assert not flags(plan).any()
+        assert np.array_equal(out_bits(o2), out_bits(ref))
+
+
+def test_back_to_back_runs_without_host_sync():
+    import torch
+    say("back to back")
+    x, dev, plan = _setup()
+    with plan:
+        s = torch.cuda.current_stream()
+        outs = [new_out(SMALL) for _ in range(3)]
+        for o in outs:
+            plan.run(dev["A"], dev["B"], dev["C"], SMALL.alpha, SMALL.beta, o, s)
+        rc, detail = plan.status(s)
+        assert rc == G.OK, detail
+        b = [out_bits(o) for o in outs]
+        assert np.array_equal(b[0], b[1]) and np.array_equal(b[0], b[2])
+        assert not flags(plan).any()
+
+
+def test_missing_producer_times_out_and_plan_recovers():
+    say("timeout")
+    x, dev, plan = _setup(timeout_ms=5)
+    with plan:
+        o = new_out(SMALL)
+        run_checked(plan, dev, SMALL, o, G.RUN_GEMM)
+        r0, t0 = 5, 7
+        h2d(plan.info.flags, np.zeros(1, dtype=np.uint32), (r0 * plan.info.T + t0) * 4)
+        plan.run(dev["A"], dev["B"], dev["C"], SMALL.alpha, SMALL.beta, o, None,
+                 G.RUN_REDUCE)
+        rc, detail = plan.status()
+        assert rc == G.ERR_TIMEOUT
+        assert detail == [G.ERR_TIMEOUT, r0, t0, 0]
+        assert not flags(plan).any()                 # status re-zeroed them
+        assert plan.status()[0] == G.OK              # and cleared the record
+        ref = new_out(SMALL)
+        run_checked(plan, dev, SMALL, ref)           # the plan runs again
+
+
+def test_stale_flag_is_a_protocol_error():
+    say("protocol")
+    x, dev, plan = _setup()
+    with plan:
+        o = new_out(SMALL)
+        run_checked(plan, dev, SMALL, o, G.RUN_GEMM)
+        r1, t1 = 2, 3
+        h2d(plan.info.flags, np.array([2], dtype=np.uint32), (r1 * plan.info.T + t1) * 4)
+        plan.run(dev["A"], dev["B"], dev["C"], SMALL.alpha, SMALL.beta, o, None,
+                 G.RUN_REDUCE)
+        rc, detail = plan.status()
+        assert rc == G.ERR_PROTOCOL and detail == [G.ERR_PROTOCOL, r1, t1, 2]
+        assert not flags(plan).any()
+
+
+# ----------------------------------------------- reduce on host-written staging
+def _reduce_only(W, M, N, dtype, order, groups, S_rmn, tile=(64, 128),
+                 materialize=0):
+    """Write S (per rank r, output [M][N]) into the staging slots, set every
+    flag, run REDUCE only, return output bits."""
+    import torch
+    if dtype == G.F32:
+        tile = (64, 64)     # the only fp32 tile
+    desc = dict(M=M, N=N, K=64, W=W, dtype=dtype, tile_m=tile[0], tile_n=tile[1],
+                order=order, groups=groups, materialize_sub=materialize)
+    with G.Plan(**desc) as plan:
+        Mc = M // W
+        # staging S[d][r][Mc][N] from S_rmn[r][d*Mc + il][j]
+        st = S_rmn.reshape(W, W, Mc, N).transpose(1, 0, 2, 3)
+        h2d(plan.info.staging, np.ascontiguousarray(st, dtype=np.float32))
+        h2d(plan.info.flags, np.ones(W * plan.info.T, dtype=np.uint32))
+        out = torch.empty((M, N), dtype=torch.int16 if dtype == G.BF16 else torch.float32,
+                          device="cuda:0")
+        plan.run(None, None, None, 1.0, 0.0, out, None, G.RUN_REDUCE)
+        rc, detail = plan.status()
+        assert rc == G.OK, detail
+        assert not flags(plan).any()
+        return out_bits(out)
+
+
+@pytest.mark.parametrize("order,groups,want", [(O.FLAT, 1, 0.0),
+                                               (O.TWO_LEVEL, 2, 3.0),
+                                               (O.TWO_LEVEL, 4, 5.0)])
+def test_reduce_order_closed_form(order, groups, want):
+    say("reduce order", order, groups)
+    v = np.array([2.0**24, 1, 1, 1, 1, 1, 1, -2.0**24], dtype=np.float32)
+    W, M, N = 8, 64, 128
+    S = np.broadcast_to(v[:, None, None], (W, M, N)).astype(np.float32)
+    for materialize in ([0, 1] if order == O.TWO_LEVEL else [0]):
+        bits = _reduce_only(W, M, N, G.F32, order, groups, S, materialize=materialize)
+        assert np.all(bits.view(np.float32) == want)
+        bits = _reduce_only(W, M, N, G.BF16, order, groups, S, materialize=materialize)
+        assert np.all(bits == O.bf16_rne(np.array([want], np.float32))[0])
+
+
+@pytest.mark.parametrize("dtype", [G.BF16, G.F32])
+@pytest.mark.parametrize("order,groups,materialize", [(O.FLAT, 1, 0), (O.TWO_LEVEL, 2, 0),
+                                                      (O.TWO_LEVEL, 4, 0),
+                                                      (O.TWO_LEVEL, 2, 1)])
+def test_reduce_random_staging_bit_exact(dtype, order, groups, materialize):
+    say("reduce random", dtype, order, groups, materialize)
+    rng = np.random.default_rng(21)
+    W, M, N = 8, 8 * 40, 256
+    S = (rng.standard_normal((W, M, N)) * np.exp(rng.uniform(-8, 8, (W, M, N)))).astype(
+        np.float32)
+    bits = _reduce_only(W, M, N, dtype, order, groups, S, tile=(128, 128),
+                        materialize=materialize)
+    want = O.reduce_emulate(S.reshape(W, M * N), order=order, groups=groups,
+                            out_bf16=(dtype == G.BF16))
+    assert np.array_equal(bits.ravel(), want.view(bits.dtype))
+
+
+def test_output_rounding_ties_w1():
+    say("rne ties")
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F808008], dtype=np.uint32)
+    W, M, N = 1, 64, 128
+    S = np.resize(ties, M * N).view(np.float32).reshape(1, M, N)
+    bits = _reduce_only(W, M, N, G.BF16, O.FLAT, 1, S)
+    assert bits.ravel()[:4].tolist() == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
+    assert np.array_equal(bits.ravel(), O.bf16_rne(S.ravel()))
