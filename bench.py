@@ -1,0 +1,246 @@
+"""Benchmark: one fused GEMM + reduce-scatter pass per step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama70b]
+
+A step is the whole hot path over one batch: the GEMM + epilogue kernel
+(scatter into staging slots, flag publish) and the flag-gated reduce, on
+W = 8 virtual ranks at the 70B-like FFN down-projection shard
+(A_r[8192,3584] x B_r[3584,8192], bias row, bf16).  Inputs are resident in
+HBM before timing starts.  Prints one JSON line.
+
+value = algorithmic FLOPs of the step (W * 2*M*N*K) / wall time per step.
+roofline: the GEMM kernel against the bf16 dense MFMA peak, with its
+duration from HIP events around each launch inside the timed region.
+cpu_baseline: the CPU oracle (fp64, all host threads) on a bounded sample
+of the same workload's output rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+METRIC = ("fused GEMM+RS TFLOP/s & MFMA util % at M=8192 N=8192 K=3584 W=8; "
+          "reduce GB/s")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_llama70b.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Hash of the GEMM kernel's sources: a stored traffic figure is valid
+    only for the code it was measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_gemm_reduce_lds_amd", "csrc")
+    for f in ("gemm_bf16.hip", "gemm_rs_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on other kernel code."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(w, elem):
+    """GEMM kernel: A + B read once, fp32 staging written once, C read once
+    (one row when broadcast).  Reduce: staging read once, out written once."""
+    gemm = w.W * w.M * w.K * elem + w.W * w.K * w.N * elem + w.W * w.M * w.N * 4
+    if w.has_c:
+        gemm += (w.N if w.ldc == 0 else w.M * w.N) * elem
+    red = w.W * w.M * w.N * 4 + w.M * w.N * elem
+    return gemm, red
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """Time the oracle (fp64 reference rows, every rank, OpenMP over rows)
+    on the first rows of the workload for about budget_s seconds."""
+    import oracle as O
+    kw = dict(dtype=O.BF16 if w.dtype == "bf16" else O.F32, alpha=w.alpha,
+              beta=w.beta, ldc=w.ldc,
+              order=O.TWO_LEVEL if w.order == "two_level" else O.FLAT,
+              groups=w.groups)
+    threads = O.num_threads()
+    rows, t = threads, 0.0
+    t0 = time.perf_counter()
+    O.reference_rows(x["A"], x["B"], x["C"], row_lo=0, row_hi=rows, **kw)
+    t = time.perf_counter() - t0
+    if t < budget_s / 3:
+        more = max(threads, int(rows * (budget_s - t) / max(t, 1e-3)) // threads * threads)
+        more = min(more, w.M - rows)
+        t1 = time.perf_counter()
+        O.reference_rows(x["A"], x["B"], x["C"], row_lo=rows, row_hi=rows + more, **kw)
+        t += time.perf_counter() - t1
+        rows += more
+    flops = rows * w.W * 2 * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 reference of output rows [0, %d) of %d (all %d ranks, "
+                      "K=%d, N=%d): %.3g GFLOP in %.1f s" % (
+                          rows, w.M, w.W, w.K, w.N, flops / 1e9, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama70b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for cpu_baseline (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="MiB: run one plain device copy of this size first "
+                         "(reference point for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (W virtual ranks on one "
+              "device); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tensor_gemm_reduce_lds_amd import gemm_rs as G
+    from tensor_gemm_reduce_lds_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    log("bench: workload", w)
+    t0 = time.perf_counter()
+    x = I.make_inputs(w, seed=args.seed)
+    log("bench: inputs generated in %.1f s" % (time.perf_counter() - t0))
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        if a is None:
+            return None
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    A, B, C = up(x["A"]), up(x["B"]), up(x["C"])
+    out = torch.empty((w.M, w.N), dtype=torch.int16 if w.dtype == "bf16" else torch.float32,
+                      device=dev)
+    plan = G.Plan(M=w.M, N=w.N, K=w.K, W=w.W,
+                  dtype=G.BF16 if w.dtype == "bf16" else G.F32,
+                  tile_m=w.tile_m, tile_n=w.tile_n,
+                  order=G.ORDER_TWO_LEVEL if w.order == "two_level" else G.ORDER_FLAT,
+                  groups=w.groups, has_c=int(w.has_c), ldc=w.ldc)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: calibration copy of %d MiB done" % args.copy_calibration)
+        del src, dst
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_GEMM)
+        if ev is not None:
+            ev[1].record(stream)
+        plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_REDUCE)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    rc, detail = plan.status(stream)
+    if rc != G.OK:
+        raise RuntimeError("warmup failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    rc, detail = plan.status(stream)
+    if rc != G.OK:
+        raise RuntimeError("timed run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+
+    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms = wall * 1e3 / args.steps
+    flops = w.flops
+    elem = w.elem_bytes
+    gemm_bytes, red_bytes = algorithmic_bytes(w, elem)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    red_gbps = red_bytes / (red_ms * 1e-3) / 1e9
+    traffic = stored_traffic() if w.name == "llama70b" else None
+    info = plan.info
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded PCG64: A~N(0,1), B~N(0,1/K), bias~N(0,0.02^2))",
+        "config": {"workload": "%s FFN down-projection shard" % w.name, "W": w.W,
+                   "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+                   "bias": ("row-broadcast" if w.ldc == 0 else "full") if w.has_c else None,
+                   "tile": "%dx%d" % (info.tile_m, info.tile_n), "order": w.order,
+                   "staging": "fp32", "parallelism": "1 GPU, %d virtual ranks" % w.W},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / peak, 4),
+                     "traffic": traffic},
+        "gemm_kernel_ms": round(gemm_ms, 4),
+        "gemm_tflops": round(gemm_tflops, 2),
+        "mfma_util_pct": round(100 * gemm_tflops / peak, 2),
+        "gemm_algorithmic_bytes": gemm_bytes,
+        "reduce_kernel_ms": round(red_ms, 4),
+        "reduce_gbps": round(red_gbps, 1),
+        "reduce_hbm_frac": round(red_gbps / PEAK_HBM_GBPS, 4),
+        "reduce_algorithmic_bytes": red_bytes,
+    }
+    plan.close()
+    del A, B, C, out
+    if args.cpu_budget > 0:
+        log("bench: timing the CPU oracle (~%.0f s)" % args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

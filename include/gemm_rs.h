@@ -84,7 +84,8 @@ extern "C" {
  *   dtype        GEMM_RS_BF16 or GEMM_RS_F32
  *   tile_m/_n    output tile (the communication unit); 0 picks a default.
  *                bf16: 256x256, 256x128, 128x128, 64x128; f32: 64x64.
- *   group_m      tile-rows per group inside a chunk (0 or 1: row-major)
+ *   group_m      tile-rows per group inside a chunk; 1: row-major;
+ *                0: the default, 4
  *   order        GEMM_RS_ORDER_*; groups = G for the two-level order
  *                (W % G == 0; ranks g*W/G .. (g+1)*W/G-1 form group g)
  *   swizzle      GEMM_RS_SWIZZLE_*

@@ -1,116 +1,165 @@
 // bf16 GEMM + reduce-scatter epilogue for gfx950.
 //
 // Workgroup b computes one BM x BN output tile of rank r = b % W (tile
-// order: tile_of_block).  Mainloop: 64-deep K steps, A and B tiles staged
-// through LDS (double buffered, 16-byte global loads, XOR-swizzled rows),
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Epilogue: alpha*acc,
-// plus beta*C on rows whose chunk this rank owns, stored as fp32 into the
-// staging slot of the row's destination chunk; then the tile's ready flag
-// is released at agent scope (page "flux实现：sm80 gemm+rs", section
-// "cutlass自定义epilogue–sm80": compute node alpha*acc + beta*C, store node
-// that scatters by destination, and a per-tile flag).
+// order: tile_of_block).
+//
+// Mainloop, per BK-deep K step:
+//   * A[BM][BK] and B[BK][BN] tiles go from HBM straight into LDS with
+//     16-byte global_load_lds (no register staging) into a ring of STAGES
+//     LDS stages; loads run STAGES-1 steps ahead of the MFMAs.  The DMA is
+//     issued from inline asm and its completion tracked by explicit vmcnt
+//     waits, so the compiler does not serialise LDS reads of one stage
+//     behind DMA still in flight into another.
+//   * A sits in LDS as [m][k] rows of 2*BK bytes; B stays row-major [k][n]
+//     as it is in memory.  Both are XOR-swizzled at 16-byte granularity
+//     (the swizzle is applied by choosing which global chunk each lane
+//     fetches, since a DMA load writes lane l at base + 16*l).
+//   * A operands come from ds_read_b128; B operands from two
+//     ds_read_b64_tr_b16 per MFMA, which transpose 4x16 bf16 blocks across
+//     16 lanes so that each lane gets 4 consecutive k of one column.
+//   * v_mfma_f32_32x32x16_bf16, fp32 accumulators.
+// Epilogue: alpha*acc, plus beta*C on rows whose chunk this rank owns,
+// stored as fp32 into the staging slot of each row's destination chunk;
+// then the tile's ready flag is released at agent scope (page "flux实现：
+// sm80 gemm+rs", section "cutlass自定义epilogue–sm80": a compute node
+// alpha*acc + beta*C, a store node that scatters by destination, and a
+// per-tile flag).
 #include "gemm_rs_internal.h"
 
 namespace gemm_rs {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int BK = 64;          // K depth of one LDS stage (elements)
-constexpr int ROW_ELEMS = BK;   // LDS row: 64 bf16 = 128 bytes = 8 chunks
+#pragma clang diagnostic ignored "-Winline-asm"
 
-// 16-byte chunk c of LDS row `row` is stored at chunk swz(row, c).  Rows
-// r and r + 8k map their chunks differently, which keeps both the 8x8 B
-// transposes and the MFMA operand reads spread over the banks.
-__device__ __forceinline__ int swz(int row, int c) {
-    return c ^ ((row ^ (row >> 3)) & 7);
+// 16 bytes per lane from global memory straight into LDS: lane l's data
+// lands at lds_base + 16*l (lds_base is wave-uniform, passed in M0).
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
-    return __uint_as_float((uint32_t)h << 16);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
-    constexpr int WM = BM / 2, WN = BN / 2;       // 2 x 2 waves
-    constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 MFMA blocks per wave
-    constexpr int A_LOADS = BM / 32;              // 16-byte A loads per thread
-    constexpr int NB = BN / 8;                    // 8-column groups of B
-    constexpr int KR = BK * BN / 8 / kThreads;    // B k-rows per thread
-    static_assert(KR == 2 || KR == 4 || KR == 8, "B tile split");
-    constexpr int STAGE = (BM + BN) * ROW_ELEMS;  // bf16 elements per stage
+// Wait until at most `pending` DMA groups of `per` loads are in flight.
+template <int PER, int MAXP>
+__device__ __forceinline__ void wait_groups(int pending) {
+    if constexpr (MAXP >= 3) { if (pending >= 3) { wait_vmcnt<3 * PER>(); return; } }
+    if constexpr (MAXP >= 2) { if (pending >= 2) { wait_vmcnt<2 * PER>(); return; } }
+    if constexpr (MAXP >= 1) { if (pending >= 1) { wait_vmcnt<PER>(); return; } }
+    wait_vmcnt<0>();
+}
 
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+// A rows are 2*BK bytes (BK/8 chunks of 16 bytes); chunk c of row m lives
+// at c ^ swa(m).  The 16 rows read by 16 lanes then cover all 64 banks once.
+template <int BK>
+__device__ __forceinline__ int swa(int m) {
+    if constexpr (BK == 64) return (m ^ (m >> 3)) & 7;
+    else return (m >> 2) & 3;
+}
+// B rows: chunk c of row k lives at c ^ swb(k).  A transpose read touches
+// 4 consecutive k rows x 4 chunks per 32 lanes; XOR with 4*(k%4) spreads
+// them over 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swb(int k) { return 4 * (k & 3); }
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr int NW = WGM * WGN;                 // waves
+    constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile
+    constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_ISSUES = A_BYTES / 1024 / NW;  // 1 KB DMA loads per wave
+    constexpr int B_ISSUES = B_BYTES / 1024 / NW;
+    constexpr int CPA = BK / 8;                   // 16-byte chunks per A row
+    constexpr int A_ROWS = 1024 / (BK * 2);       // A rows per 1 KB
+    constexpr int CPR = BN / 8;                   // 16-byte chunks per B row
+    constexpr int B_ROWS = 1024 / (BN * 2);       // B rows per 1 KB
+    constexpr int PER = A_ISSUES + B_ISSUES;      // DMA loads per lane per stage
+    static_assert(A_ISSUES * NW * 1024 == A_BYTES && B_ISSUES * NW * 1024 == B_BYTES, "");
+    static_assert(CPR >= 16, "B swizzle needs rows of at least 16 chunks");
+
+    extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
+    lds_char *smem = (lds_char *)smem_generic;
+    const uint32_t smem_base = (uint32_t)(size_t)smem;
 
     const TileGeom &g = a.g;
     int32_t r, t;
     tile_of_block(g, blockIdx.x, &r, &t);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
 
     const uint16_t *A = (const uint16_t *)a.A + (int64_t)r * g.M * g.K;
     const uint16_t *B = (const uint16_t *)a.B + (int64_t)r * g.K * g.N;
-    const int64_t row0 = (int64_t)tm * BM;
-    const int64_t col0 = (int64_t)tn * BN;
+    const int64_t row0 = (int64_t)tm * BM, col0 = (int64_t)tn * BN;
 
-    // per-thread global source pointers (k offset added per stage)
-    const uint16_t *a_src[A_LOADS];
+    // ---- per-lane DMA sources (k offset added per step) ----
+    const uint16_t *a_src[A_ISSUES];
 #pragma unroll
-    for (int p = 0; p < A_LOADS; ++p) {
-        int64_t row = row0 + p * 32 + (tid >> 3);
-        if (row > g.M - 1) row = g.M - 1;   // ragged M: read a valid row
-        a_src[p] = A + row * g.K + (tid & 7) * 8;
+    for (int i = 0; i < A_ISSUES; ++i) {
+        const int m = (i * NW + wave) * A_ROWS + lane / CPA;
+        int64_t row = row0 + m;
+        if (row > g.M - 1) row = g.M - 1;   // ragged M: fetch a valid row
+        a_src[i] = A + row * g.K + ((lane % CPA) ^ swa<BK>(m)) * 8;
     }
-    const int nb = tid % NB, kb = tid / NB;
-    const uint16_t *b_src = B + (int64_t)(kb * KR) * g.N + col0 + nb * 8;
-
-    u32x4_t a_reg[A_LOADS];
-    u32x4_t b_reg[KR];
-
-    auto load_global = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * BK;
+    const uint16_t *b_src[B_ISSUES];
 #pragma unroll
-        for (int p = 0; p < A_LOADS; ++p)
-            a_reg[p] = *(const u32x4_t *)(a_src[p] + k0);
+    for (int i = 0; i < B_ISSUES; ++i) {
+        const int k = (i * NW + wave) * B_ROWS + lane / CPR;
+        b_src[i] = B + (int64_t)k * g.N + col0 + ((lane % CPR) ^ swb(k)) * 8;
+    }
+
+    auto issue = [&](int kt, int buf) {
+        const uint32_t As = smem_base + buf * STAGE;
+        const uint32_t Bs = As + A_BYTES;
+        const int64_t ka = (int64_t)kt * BK, kb = (int64_t)kt * BK * g.N;
 #pragma unroll
-        for (int e = 0; e < KR; ++e)
-            b_reg[e] = *(const u32x4_t *)(b_src + (k0 + e) * g.N);
+        for (int i = 0; i < A_ISSUES; ++i)
+            dma16(a_src[i] + ka, As + (i * NW + wave) * 1024);
+#pragma unroll
+        for (int i = 0; i < B_ISSUES; ++i)
+            dma16(b_src[i] + kb, Bs + (i * NW + wave) * 1024);
     };
 
-    auto store_lds = [&](int buf) {
-        uint16_t *As = lds + buf * STAGE;
-        uint16_t *Bs = As + BM * ROW_ELEMS;
+    // ---- per-lane LDS read offsets (bytes, within a stage) ----
+    int a_off[FM][BK / 16];
 #pragma unroll
-        for (int p = 0; p < A_LOADS; ++p) {
-            const int row = p * 32 + (tid >> 3);
-            *(u32x4_t *)(As + row * ROW_ELEMS + swz(row, tid & 7) * 8) = a_reg[p];
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int m = wm * WM + i * 32 + (lane & 31);
+            const int c = 2 * ks + (lane >> 5);
+            a_off[i][ks] = m * (BK * 2) + ((c ^ swa<BK>(m)) << 4);
         }
-        // 8x8 (KR x 8) transpose: B[k][n] -> Bs[n][k] (k contiguous)
+    // transpose-read source lane: row kbase + e, columns 4q..4q+3 of its
+    // 16-column group (e = (lane%16)/4, q = lane%4)
+    int b_off[FN][BK / 16][2];
+    {
+        const int grp = lane >> 4, i16 = lane & 15;
+        const int e = i16 >> 2, q = i16 & 3;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int n = nb * 8 + q;
-            const int w = q >> 1, sh = (q & 1) * 16;
-            uint32_t v[KR];
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < KR; ++e) v[e] = (b_reg[e][w] >> sh) & 0xffffu;
-            const int kofs = kb * KR;              // element offset in the row
-            uint16_t *dst = Bs + n * ROW_ELEMS + swz(n, kofs >> 3) * 8 + (kofs & 7);
-            if constexpr (KR == 8) {
-                u32x4_t o = {v[0] | (v[1] << 16), v[2] | (v[3] << 16),
-                             v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-                *(u32x4_t *)dst = o;
-            } else if constexpr (KR == 4) {
-                u32x2_t o = {v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
-                *(u32x2_t *)dst = o;
-            } else {
-                *(uint32_t *)dst = v[0] | (v[1] << 16);
-            }
-        }
-    };
+            for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + e;
+                    const int n = wn * WN + j * 32 + 16 * (grp & 1) + 4 * q;
+                    b_off[j][ks][h] = A_BYTES + k * (BN * 2) +
+                                      (((n >> 3) ^ swb(k)) << 4) + ((n & 7) << 1);
+                }
+    }
 
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -121,93 +170,123 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     auto compute = [&](int buf) {
-        const uint16_t *As = lds + buf * STAGE;
-        const uint16_t *Bs = As + BM * ROW_ELEMS;
+        lds_char *S = smem + buf * STAGE;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks * 2 + (lane >> 5);
             bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * WM + i * 32 + (lane & 31);
-                af[i] = *(const bf16x8_t *)(As + row * ROW_ELEMS + swz(row, c) * 8);
-            }
+            for (int i = 0; i < FM; ++i)
+                af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(S + a_off[i][ks]);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int n = wn * WN + j * 32 + (lane & 31);
-                bfr[j] = *(const bf16x8_t *)(Bs + n * ROW_ELEMS + swz(n, c) * 8);
+                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][0]));
+                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][1]));
+                i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                bfr[j] = __builtin_bit_cast(bf16x8_t, both);
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    // operands swapped: the block comes out transposed, so a
+                    // lane holds one output row and runs of 4 columns
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i],
+                                                                        acc[i][j], 0, 0, 0);
         }
     };
 
     const int KT = (int)(g.K / BK);
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) issue(s, s);
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_global(kt + 1);
-        compute(cur);
-        if (kt + 1 < KT) store_lds(cur ^ 1);
+        // wait until this wave's DMA for step kt has landed (later steps
+        // may stay in flight); the barrier makes every wave's data visible
+        // and frees the stage read in step kt-1 for the next issue
+        const int ahead = KT - 1 - kt;
+        wait_groups<PER, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
         __syncthreads();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+        compute(kt % STAGES);
     }
 
     // ---- epilogue: D = alpha*acc (+ beta*C on owned rows), scatter ----
-    // 32x32 accumulator layout: lane holds column (lane & 31); register v
-    // holds row 8*(v/4) + 4*(lane/32) + (v%4) of the 32x32 block.
+    // Transposed 32x32 accumulator layout: lane holds output row (lane & 31)
+    // of the block; registers 4q..4q+3 hold its columns 8q + 4*(lane/32)
+    // + 0..3.  Each lane therefore writes 16-byte runs of one staging row.
     const uint16_t *Cp = (const uint16_t *)a.C;
     const float alpha = a.alpha, beta = a.beta;
+    const int h4 = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = row0 + wm * WM + i * 32 + 8 * (v >> 2) +
-                                4 * (lane >> 5) + (v & 3);
-            if (row >= g.M) continue;
+        const int64_t row = row0 + wm * WM + i * 32 + (lane & 31);
+        if (row < g.M) {
             const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
             const bool own_c = a.has_c && d == r;
             float *dst = a.staging +
-                         (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N;
+                         (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
+                         col0 + wn * WN + h4;
+            const uint16_t *crow = own_c ? Cp + row * a.ldc + col0 + wn * WN + h4 : nullptr;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t col = col0 + wn * WN + j * 32 + (lane & 31);
-                float x = alpha * acc[i][j][v];
-                if (own_c) x += beta * bf16_bits_to_float(Cp[row * a.ldc + col]);
-                __builtin_nontemporal_store(x, dst + col);
-            }
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = j * 32 + 8 * q;       // column offset in the wave tile
+                    f32x4_t x;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
+                    if (own_c) {
+                        const uint2 cb = *(const uint2 *)(crow + c);
+                        x[0] += beta * __uint_as_float(cb.x << 16);
+                        x[1] += beta * __uint_as_float(cb.x & 0xffff0000u);
+                        x[2] += beta * __uint_as_float(cb.y << 16);
+                        x[3] += beta * __uint_as_float(cb.y & 0xffff0000u);
+                    }
+                    // a plain (write-back) store: the four 16-byte runs of a
+                    // 128-byte line come from four instructions and merge in
+                    // L2; a streaming hint here costs ~20%
+                    *(f32x4_t *)(dst + c) = x;
+                }
         }
     }
 
     // ---- publish: all stores of this tile, then flag[r][t] = 1 ----
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        if (a.trace) a.trace[blockIdx.x] = t;
+    // With a concurrent consumer the flag is an agent-scope release (the
+    // tile's stores are written back past this XCD's L2 first).  When the
+    // consumer is stream-ordered after this kernel, the kernel boundary
+    // already makes the stores visible and the flag is a plain store.
+    if (a.release_flags) {
+        __threadfence();
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid == 0 && a.trace) a.trace[blockIdx.x] = t;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
-    constexpr size_t lds_bytes = 2 * (BM + BN) * BK * sizeof(uint16_t);
+    constexpr size_t lds_bytes = (size_t)STAGES * (BM + BN) * BK * 2;
+    static_assert(lds_bytes <= 160 * 1024, "LDS");
     static bool configured = false;
     if (!configured) {
         hipError_t e = hipFuncSetAttribute(
-            (const void *)gemm_bf16_kernel<BM, BN>,
+            (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;
         configured = true;
     }
     const int64_t blocks = (int64_t)a.g.W * a.g.T;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3((unsigned)blocks),
-                       dim3(kThreads), lds_bytes, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>),
+                       dim3((unsigned)blocks), dim3(64 * WGM * WGN), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -220,10 +299,15 @@ bool bf16_tile_supported(int32_t bm, int32_t bn) {
 
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int bm = a.g.BM, bn = a.g.BN;
-    if (bm == 256 && bn == 256) return launch_tile<256, 256>(a, s);
-    if (bm == 256 && bn == 128) return launch_tile<256, 128>(a, s);
-    if (bm == 128 && bn == 128) return launch_tile<128, 128>(a, s);
-    if (bm == 64 && bn == 128) return launch_tile<64, 128>(a, s);
+#ifndef GEMM_RS_BK
+#define GEMM_RS_BK 64
+#define GEMM_RS_STAGES 2
+#endif
+    constexpr int BKc = GEMM_RS_BK, ST = GEMM_RS_STAGES;
+    if (bm == 256 && bn == 256) return launch_tile<256, 256, BKc, ST, 2, 4>(a, s);
+    if (bm == 256 && bn == 128) return launch_tile<256, 128, BKc, ST, 2, 2>(a, s);
+    if (bm == 128 && bn == 128) return launch_tile<128, 128, BKc, ST, 2, 2>(a, s);
+    if (bm == 64 && bn == 128) return launch_tile<64, 128, BKc, ST, 1, 2>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -76,11 +76,17 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         __builtin_nontemporal_store(x, dst + col);
     }
 
-    __threadfence();
+    // flag publish: agent-scope release for a concurrent consumer, a plain
+    // store when the consumer is stream-ordered after this kernel
+    if (a.release_flags) __threadfence();
     __syncthreads();
     if (tid == 0) {
-        __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (a.release_flags)
+            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         if (a.trace) a.trace[blockIdx.x] = t;
     }
 }

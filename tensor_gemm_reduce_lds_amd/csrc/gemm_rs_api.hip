@@ -150,7 +150,9 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     if (rc != GEMM_RS_OK) return rc;
     d.tile_m = bm;
     d.tile_n = bn;
-    if (d.group_m == 0) d.group_m = 1;
+    // default: groups of 4 tile-rows walked column by column, so the ~32
+    // tiles a rank has in flight on its XCD share 4 A and 8 B panels in L2
+    if (d.group_m == 0) d.group_m = 4;
     if (d.order == GEMM_RS_ORDER_FLAT) d.groups = 1;
     if (d.timeout_ms == 0) d.timeout_ms = 1000;
 
@@ -261,6 +263,8 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         a.staging = p->staging;
         a.flags = p->flags;
         a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
+        // the reduce is launched after this kernel on the same stream
+        a.release_flags = 0;
         hipError_t e = p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(a, s)
                                                   : launch_gemm_f32(a, s);
         if (e != hipSuccess) return GEMM_RS_ERR_HIP;

@@ -71,6 +71,7 @@ struct GemmArgs {
     float *staging;      // [W][W][Mc][N]
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
+    int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
 };
 
 struct ReduceArgs {
