@@ -275,6 +275,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         r.order = p->d.order;
         r.groups = p->d.groups;
         r.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
+        r.acquire = 0;   // the GEMM kernel ran before on this stream
         r.units_per_tile = p->units_per_tile;
         r.timeout_ticks = p->timeout_ticks;
         r.staging = p->staging;

@@ -8,8 +8,11 @@
 
 namespace gemm_rs {
 
-// Reduce work unit: RB output rows of one tile.
-constexpr int kReduceRows = 32;
+// Reduce work unit: kReduceRows output rows of one tile.
+#ifndef GEMM_RS_REDUCE_ROWS
+#define GEMM_RS_REDUCE_ROWS 32
+#endif
+constexpr int kReduceRows = GEMM_RS_REDUCE_ROWS;
 constexpr int kThreads = 256;
 
 // Geometry the kernels need to place tiles.
@@ -78,6 +81,7 @@ struct ReduceArgs {
     TileGeom g;
     int32_t order, groups;   // groups == 1 for flat
     int32_t keep_flags;
+    int32_t acquire;         // 1: producers may run concurrently
     int32_t units_per_tile;  // BM / kReduceRows
     uint64_t timeout_ticks;  // device wall-clock ticks
     const float *staging;

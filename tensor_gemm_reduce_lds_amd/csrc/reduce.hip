@@ -32,10 +32,12 @@ __device__ void record_error(int32_t *err, int code, int32_t r, int32_t t, uint3
 
 // Wait until *f == 1.  Returns 0, or the error code after recording it.
 __device__ int wait_ready(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
-                          int32_t r, int32_t t) {
+                          int32_t r, int32_t t, bool acquire) {
     const uint64_t t0 = wall_clock64();
     for (;;) {
-        const uint32_t v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t v =
+            acquire ? __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                    : __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (v == 1u) return 0;
         if (v != 0u) {
             record_error(err, GEMM_RS_ERR_PROTOCOL, r, t, v);
@@ -49,22 +51,26 @@ __device__ int wait_ready(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
     }
 }
 
-// Threads [first, first+count) each wait on one flag; true if all ready.
-// Ends with a barrier and an agent-scope acquire fence in every thread, so
-// loads issued afterwards see what the producers stored before releasing.
-__device__ bool wait_flags(uint32_t *base, int64_t stride,
-                           int count, uint64_t timeout_ticks, int32_t *err,
-                           int32_t rank0, int32_t tile) {
+// Threads [0, count) each wait on one flag; true if all ready.  With
+// `acquire` (producers may still be running) the waits are agent-scope
+// acquires and every thread then takes an acquire fence, so loads issued
+// afterwards see what the producers stored before releasing.  Without it
+// (producers finished in an earlier kernel on the stream) the stream
+// order already makes their stores visible and plain loads suffice.
+__device__ bool wait_flags(uint32_t *base, int64_t stride, int count,
+                           uint64_t timeout_ticks, int32_t *err, int32_t rank0,
+                           int32_t tile, bool acquire) {
     __shared__ int failed;
     if (threadIdx.x == 0) failed = 0;
     __syncthreads();
     const int i = threadIdx.x;
     if (i < count) {
-        if (wait_ready(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile))
+        if (wait_ready(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile,
+                       acquire))
             atomicOr(&failed, 1);
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return failed == 0;
 }
 
@@ -120,6 +126,35 @@ __device__ __forceinline__ f32x4_t ordered_sum(const float *S, int64_t stride, i
     }
 }
 
+// Two elements at once (all 2*W loads issued before any add).
+template <int WT>
+__device__ __forceinline__ void ordered_sum2(const float *S, const float *S2, int64_t stride,
+                                             int W, int L, f32x4_t *y_out, f32x4_t *y2_out) {
+    if constexpr (WT > 0) {
+        f32x4_t v[WT], u[WT];
+#pragma unroll
+        for (int q = 0; q < WT; ++q) {
+            v[q] = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
+            u[q] = __builtin_nontemporal_load((const f32x4_t *)(S2 + q * stride));
+        }
+        f32x4_t y = v[0], s = v[0], y2 = u[0], s2 = u[0];
+#pragma unroll
+        for (int q = 0; q < WT; ++q) {
+            s = (q % L == 0) ? v[q] : s + v[q];
+            s2 = (q % L == 0) ? u[q] : s2 + u[q];
+            if (q % L == L - 1) {
+                y = (q / L == 0) ? s : y + s;
+                y2 = (q / L == 0) ? s2 : y2 + s2;
+            }
+        }
+        *y_out = y;
+        *y2_out = y2;
+    } else {
+        *y_out = ordered_sum<0>(S, stride, W, L);
+        *y2_out = ordered_sum<0>(S2, stride, W, L);
+    }
+}
+
 // One-stage reduce: flags -> out.
 template <int WT, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
@@ -128,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const int32_t t = (int32_t)(blockIdx.x / U), slab = (int32_t)(blockIdx.x % U);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
-    if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t)) return;
+    if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t, a.acquire)) return;
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(&a.counters[t], 1u);
         if (old == (uint32_t)U - 1) {   // every unit of the tile has passed
@@ -144,16 +179,26 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     int64_t lo, hi;
     unit_rows(g, tm, slab, &lo, &hi);
     const int W = g.W, L = W / a.groups;
-    const int C4 = g.BN / 4;
-    const int64_t n4 = (hi - lo) * C4;
+    const int C4 = g.BN / 4;                  // float4 per tile row
+    const int RPP = kThreads / C4;            // rows per pass
+    const int c4 = threadIdx.x % C4;
+    const int64_t col = (int64_t)tn * g.BN + c4 * 4;
     const int64_t stride = g.Mc * g.N;
-    for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
-        const int64_t row = lo + e / C4;
-        const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
+    // two rows per thread per iteration: 2*W independent 16-byte loads
+    for (int64_t row = lo + threadIdx.x / C4; row < hi; row += 2 * RPP) {
+        const int64_t row2 = row + RPP;
         const int64_t d = row / g.Mc;
         const float *S = a.staging + ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
-        const f32x4_t y = ordered_sum<WT>(S, stride, W, L);
-        store_out4(a.out, row * g.N + col, y, OUT_BF16);
+        if (row2 < hi) {
+            const int64_t d2 = row2 / g.Mc;
+            const float *S2 = a.staging + ((d2 * W) * g.Mc + (row2 - d2 * g.Mc)) * g.N + col;
+            f32x4_t y, y2;
+            ordered_sum2<WT>(S, S2, stride, W, L, &y, &y2);
+            store_out4(a.out, row * g.N + col, y, OUT_BF16);
+            store_out4(a.out, row2 * g.N + col, y2, OUT_BF16);
+        } else {
+            store_out4(a.out, row * g.N + col, ordered_sum<WT>(S, stride, W, L), OUT_BF16);
+        }
     }
 }
 
@@ -169,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.flags + (int64_t)grp * L * g.T + t, g.T, L,
-                    a.timeout_ticks, a.err, grp * L, t))
+                    a.timeout_ticks, a.err, grp * L, t, a.acquire))
         return;
     if (threadIdx.x == 0) {
         uint32_t *cnt = &a.counters[(int64_t)grp * g.T + t];
@@ -215,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.sub_flags + unit, per_group, G, a.timeout_ticks,
-                    a.err, 0, t))
+                    a.err, 0, t, a.acquire))
         return;
     // a sub-flag has exactly one consumer: reset it right after the wait
     if (threadIdx.x < G && !a.keep_flags)
