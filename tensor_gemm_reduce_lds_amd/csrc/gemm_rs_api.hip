@@ -165,8 +165,11 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     g.tiles_m = (int32_t)((d.M + bm - 1) / bm);
     g.tiles_n = (int32_t)(d.N / bn);
     g.T = g.tiles_m * g.tiles_n;
-    g.group_m = d.group_m;
+    // more tile-rows per group than the matrix has changes nothing
+    g.group_m = d.group_m < g.tiles_m ? d.group_m : g.tiles_m;
     g.swizzle = d.swizzle;
+    g.bm_shift = 0;
+    while ((1 << g.bm_shift) < bm) ++g.bm_shift;
     p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;
 
     if (hipGetDevice(&p->device) != hipSuccess) { free(p); return GEMM_RS_ERR_HIP; }

@@ -19,12 +19,16 @@ constexpr int kThreads = 256;
 struct TileGeom {
     int64_t M, N, K, Mc;
     int32_t W, BM, BN, tiles_m, tiles_n, T, group_m, swizzle;
+    int32_t bm_shift;    // log2(BM)
 };
+
+// All tile-order arithmetic is 32-bit: b < W*T < 2^31 and d*Mc < M < 2^31
+// (the plan rejects larger problems), and BM is a power of two.
 
 // First tile-row whose first row lies in chunk d: ceil(d*Mc / BM), clipped.
 __host__ __device__ inline int32_t chunk_first_tile_row(const TileGeom &g, int32_t d) {
-    int64_t v = ((int64_t)d * g.Mc + g.BM - 1) / g.BM;
-    return (int32_t)(v < g.tiles_m ? v : g.tiles_m);
+    const uint32_t v = ((uint32_t)d * (uint32_t)g.Mc + (uint32_t)g.BM - 1u) >> g.bm_shift;
+    return (int32_t)(v < (uint32_t)g.tiles_m ? v : (uint32_t)g.tiles_m);
 }
 
 __host__ __device__ inline int32_t dest_chunk(const TileGeom &g, int32_t r, int32_t s) {
@@ -37,30 +41,32 @@ __host__ __device__ inline int32_t dest_chunk(const TileGeom &g, int32_t r, int3
 // Rank r walks destination chunks dest(r, 0..W-1); chunk d holds the
 // tile-rows [first(d), first(d+1)); inside a chunk, tile-rows are grouped
 // by group_m and a group is walked column by column, rows inside a column.
-__host__ __device__ inline void tile_of_block(const TileGeom &g, int64_t b,
+__host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
                                               int32_t *rank, int32_t *tile) {
-    const int32_t r = (int32_t)(b % g.W);
-    int64_t k = b / g.W;
-    int32_t tm = 0, tn = 0;
+    const uint32_t W = (uint32_t)g.W, tn_count = (uint32_t)g.tiles_n;
+    const uint32_t r = b % W;
+    uint32_t k = b / W;
+    uint32_t tm = 0, tn = 0;
     for (int32_t s = 0; s < g.W; ++s) {
-        const int32_t d = dest_chunk(g, r, s);
-        const int32_t lo = chunk_first_tile_row(g, d);
-        const int32_t rows = chunk_first_tile_row(g, d + 1) - lo;
-        const int64_t n = (int64_t)rows * g.tiles_n;
+        const int32_t d = dest_chunk(g, (int32_t)r, s);
+        const uint32_t lo = (uint32_t)chunk_first_tile_row(g, d);
+        const uint32_t rows = (uint32_t)chunk_first_tile_row(g, d + 1) - lo;
+        const uint32_t n = rows * tn_count;
         if (k < n) {
-            const int32_t gm = g.group_m;
-            const int64_t per_group = (int64_t)gm * g.tiles_n;
-            const int32_t grp = (int32_t)(k / per_group);
-            const int32_t q = (int32_t)(k - (int64_t)grp * per_group);
-            const int32_t grp_rows = (rows - grp * gm) < gm ? (rows - grp * gm) : gm;
+            const uint32_t gm = (uint32_t)g.group_m;
+            const uint32_t per_group = gm * tn_count;
+            const uint32_t grp = k / per_group;
+            const uint32_t q = k - grp * per_group;
+            const uint32_t left = rows - grp * gm;
+            const uint32_t grp_rows = left < gm ? left : gm;
             tn = q / grp_rows;
-            tm = lo + grp * gm + q % grp_rows;
+            tm = lo + grp * gm + (q - tn * grp_rows);
             break;
         }
         k -= n;
     }
-    *rank = r;
-    *tile = tm * g.tiles_n + tn;
+    *rank = (int32_t)r;
+    *tile = (int32_t)(tm * tn_count + tn);
 }
 
 struct GemmArgs {

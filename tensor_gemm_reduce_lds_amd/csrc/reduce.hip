@@ -286,7 +286,7 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= (int64_t)g.W * g.T) return;
     int32_t r, t;
-    tile_of_block(g, b, &r, &t);
+    tile_of_block(g, (uint32_t)b, &r, &t);
     trace[b] = t;
 }
 
