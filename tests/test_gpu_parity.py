@@ -208,3 +208,66 @@ def test_integer_inputs_bit_exact_everywhere(name):
     for i in rows:
         em = O.emulate_rows(x["A"], x["B"], x["C"], row_lo=i, row_hi=i + 1, **kw)
         assert np.array_equal(bits[i], em[0].view(bits.dtype)), i
+
+
+# ------------------------------------------------------------- edge cases
+EDGE = [
+    # non-power-of-two W: the reduce's runtime-W path
+    ("w3", I.with_shape(W70["llama8b"], W=3, M=3 * 100, N=256, K=128,
+                        tile_m=128, tile_n=128), {}),
+    # many ranks: 64 slots per element, Mc = 2 (every tile straddles chunks)
+    ("w64", I.with_shape(W70["llama8b"], W=64, M=128, N=128, K=64,
+                         tile_m=64, tile_n=128), {}),
+    # two-level with 1, 4 and 8 groups (G=1 and G=W are the flat order)
+    ("g1", I.with_shape(W70["ragged_2lvl"], M=8 * 40, N=256, K=128, groups=1,
+                        tile_m=128, tile_n=128), {}),
+    ("g4", I.with_shape(W70["ragged_2lvl"], M=8 * 40, N=256, K=128, groups=4,
+                        tile_m=128, tile_n=128), {}),
+    ("g8_mat", I.with_shape(W70["ragged_2lvl"], M=8 * 40, N=256, K=128, groups=8,
+                            tile_m=128, tile_n=128), dict(materialize_sub=1)),
+    ("g4_mat_decode", I.with_shape(W70["ragged_2lvl"], M=64, N=512, K=256, groups=4,
+                                   tile_m=64, tile_n=128), dict(materialize_sub=1)),
+    # fp32 with several tiles and a ragged last tile-row (M = 4*50)
+    ("f32_ragged", I.with_shape(W70["tiny_f32"], W=4, M=200, N=192, K=128), {}),
+    # fp32 with a full C matrix and alpha/beta
+    ("f32_fullc", I.with_shape(W70["tiny_f32"], W=2, M=128, N=128, K=64, has_c=True,
+                               ldc=128, alpha=0.5, beta=2.0, c_std=1.0), {}),
+    # group_m far beyond the tile-row count (clamped: same order)
+    ("group_big", I.with_shape(W70["llama8b"], W=8, M=800, N=512, K=64,
+                               tile_m=256, tile_n=256), dict(group_m=1000)),
+    # single K step
+    ("k64", I.with_shape(W70["llama70b"], W=8, M=512, N=512, K=64,
+                         tile_m=256, tile_n=256), {}),
+]
+
+
+@pytest.mark.parametrize("name,w,over", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_full_parity(name, w, over):
+    got, ref, _ = _run_small(w, **over)
+    mx, rf = check_tolerance(got, ref, w.dtype)
+    say("  max_norm_err %.3e rel_F %.3e" % (mx, rf))
+
+
+def test_edge_tile_orders_bit_exact():
+    for name, w, over in EDGE:
+        with G.Plan(**desc_fields(w, **over)) as plan:
+            assert np.array_equal(plan.tile_order(), geometry(w, plan).trace()), name
+
+
+@pytest.mark.parametrize("tile", [(256, 128), (128, 128)])
+def test_llama70b_other_tiles_sampled(tile):
+    """The 70B-like shard with the smaller tile shapes (sampled elements)."""
+    w = I.with_shape(W70["llama70b"], tile_m=tile[0], tile_n=tile[1])
+    rng = np.random.default_rng(5)
+    x = I.make_inputs(w)
+    say("70b tile", tile)
+    dev = to_device(x, w)
+    with G.Plan(**desc_fields(w)) as plan:
+        out = new_out(w)
+        run_checked(plan, dev, w, out)
+        got = out_to_f64(out, w)
+    del dev
+    ii = rng.integers(0, w.M, size=2000)
+    jj = rng.integers(0, w.N, size=2000)
+    ref = O.reference_elems(x["A"], x["B"], x["C"], ii=ii, jj=jj, **oracle_kw(w))
+    check_tolerance(got[ii, jj], ref, w.dtype)
