@@ -71,6 +71,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             "libgemm_rs.so is not built (%s); run "
             "`python -m tensor_gemm_reduce_lds_amd.build`" % path)
+    # One HIP runtime per process: torch ships its own libamdhip64, and the
+    # device pointers and streams it hands out are only valid in that
+    # instance.  Loading torch first makes this library bind to it instead
+    # of pulling a second runtime from /opt/rocm.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
     lib.gemm_rs_plan.argtypes = [ctypes.POINTER(gemm_rs_desc_t), ctypes.POINTER(vp)]
