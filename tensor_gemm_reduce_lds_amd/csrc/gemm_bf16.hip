@@ -94,7 +94,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 
     const TileGeom &g = a.g;
     int32_t r, t;
-    tile_of_block(g, blockIdx.x, &r, &t);
+    const uint32_t b = a.b_offset + blockIdx.x;
+    tile_of_block(g, b, &r, &t);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0 && a.trace) a.trace[blockIdx.x] = t;
+    if (tid == 0 && a.trace) a.trace[b] = t;
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
@@ -284,7 +285,7 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         configured = true;
     }
-    const int64_t blocks = (int64_t)a.g.W * a.g.T;
+    const int64_t blocks = a.n_blocks;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>),
                        dim3((unsigned)blocks), dim3(64 * WGM * WGN), lds_bytes, s, a);
     return hipGetLastError();

@@ -19,7 +19,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
 
     const TileGeom &g = a.g;
     int32_t r, t;
-    tile_of_block(g, blockIdx.x, &r, &t);
+    const uint32_t b = a.b_offset + blockIdx.x;
+    tile_of_block(g, b, &r, &t);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         else
             __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        if (a.trace) a.trace[blockIdx.x] = t;
+        if (a.trace) a.trace[b] = t;
     }
 }
 
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
 
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
     if (a.g.BM != BM || a.g.BN != BN) return hipErrorInvalidValue;
-    const int64_t blocks = (int64_t)a.g.W * a.g.T;
+    const int64_t blocks = a.n_blocks;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

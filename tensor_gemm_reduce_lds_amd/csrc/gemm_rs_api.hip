@@ -11,6 +11,12 @@
 
 using namespace gemm_rs;
 
+// slices of the last tile-order step in the overlapped-reduce path
+#ifndef GEMM_RS_SLICES
+#define GEMM_RS_SLICES 4
+#endif
+constexpr int kSlices = GEMM_RS_SLICES;
+
 struct gemm_rs_plan_s {
     gemm_rs_desc_t d;        // resolved (tiles, group_m, timeout filled in)
     TileGeom g;
@@ -27,6 +33,11 @@ struct gemm_rs_plan_s {
     int32_t *trace;          // [W*T]
     int64_t staging_bytes, flags_bytes, counters_bytes, sub_bytes,
         sub_flags_bytes, trace_bytes;
+    // overlapped reduce: an auxiliary stream (default priority) and events
+    hipStream_t aux;
+    hipEvent_t slice_done[kSlices];
+    hipEvent_t aux_done;
+    bool uniform_chunks;     // every chunk owns the same number of tiles
 };
 
 namespace {
@@ -106,6 +117,10 @@ void free_plan(gemm_rs_plan_s *p) {
     hipFree(p->sub_flags);
     hipFree(p->err);
     hipFree(p->trace);
+    for (int i = 0; i < kSlices; ++i)
+        if (p->slice_done[i]) hipEventDestroy(p->slice_done[i]);
+    if (p->aux_done) hipEventDestroy(p->aux_done);
+    if (p->aux) hipStreamDestroy(p->aux);
     if (switched) hipSetDevice(cur);
     free(p);
 }
@@ -196,6 +211,17 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
         if (e == hipSuccess)
             e = hipMalloc(&p->sub_counters, p->counters_bytes * d.groups);
     }
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
+    for (int i = 0; i < kSlices && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&p->slice_done[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->aux_done, hipEventDisableTiming);
+    {
+        const int32_t n0 = chunk_first_tile_row(g, 1) - chunk_first_tile_row(g, 0);
+        p->uniform_chunks = true;
+        for (int32_t dd = 1; dd < g.W; ++dd)
+            if (chunk_first_tile_row(g, dd + 1) - chunk_first_tile_row(g, dd) != n0)
+                p->uniform_chunks = false;
+    }
     // flags are zeroed once, here; runs keep them at 0 between passes
     if (e == hipSuccess) e = clear_protocol_state(p, nullptr);
     if (e == hipSuccess) e = hipMemset(p->trace, 0xff, p->trace_bytes);
@@ -243,7 +269,8 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
                 uint32_t run_flags) {
     if (!p) return GEMM_RS_ERR_INVALID_ARG;
     const uint32_t known = GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE |
-                           GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES;
+                           GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES |
+                           GEMM_RS_OVERLAP_REDUCE;
     if (run_flags & ~known) return GEMM_RS_ERR_INVALID_ARG;
     const bool do_gemm = run_flags & GEMM_RS_RUN_GEMM;
     const bool do_reduce = run_flags & GEMM_RS_RUN_REDUCE;
@@ -256,39 +283,79 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     if (do_reduce && (!out || !aligned16(out))) return GEMM_RS_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
 
-    if (do_gemm) {
-        GemmArgs a;
-        a.g = p->g;
-        a.A = A; a.B = B; a.C = C;
-        a.ldc = p->d.ldc;
-        a.has_c = p->d.has_c;
-        a.alpha = alpha; a.beta = beta;
-        a.staging = p->staging;
-        a.flags = p->flags;
-        a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
-        // the reduce is launched after this kernel on the same stream
-        a.release_flags = 0;
-        hipError_t e = p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(a, s)
-                                                  : launch_gemm_f32(a, s);
-        if (e != hipSuccess) return GEMM_RS_ERR_HIP;
+    GemmArgs a;
+    a.g = p->g;
+    a.A = A; a.B = B; a.C = C;
+    a.ldc = p->d.ldc;
+    a.has_c = p->d.has_c;
+    a.alpha = alpha; a.beta = beta;
+    a.staging = p->staging;
+    a.flags = p->flags;
+    a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
+    // every consumer runs after the producing launch completes (same stream
+    // or an event dependency), so flags are published with plain stores
+    a.release_flags = 0;
+    a.b_offset = 0;
+    a.n_blocks = (uint32_t)((int64_t)p->g.W * p->g.T);
+    auto gemm = [&](uint32_t b_lo, uint32_t b_hi, hipStream_t st) {
+        GemmArgs x = a;
+        x.b_offset = b_lo;
+        x.n_blocks = b_hi - b_lo;
+        if (x.n_blocks == 0) return hipSuccess;
+        return p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(x, st) : launch_gemm_f32(x, st);
+    };
+
+    ReduceArgs r;
+    r.g = p->g;
+    r.order = p->d.order;
+    r.groups = p->d.groups;
+    r.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
+    r.acquire = 0;
+    r.units_per_tile = p->units_per_tile;
+    r.timeout_ticks = p->timeout_ticks;
+    r.staging = p->staging;
+    r.out = out;
+    r.flags = p->flags;
+    r.counters = p->counters;
+    r.err = p->err;
+    r.sub = p->sub;
+    r.sub_flags = p->sub_flags;
+    r.k_lo = r.k_hi = 0;
+
+    const bool overlap = (run_flags & GEMM_RS_OVERLAP_REDUCE) && do_gemm && do_reduce &&
+                         p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST &&
+                         !p->d.materialize_sub && p->uniform_chunks;
+    hipError_t e = hipSuccess;
+    if (overlap) {
+        // rank d's own chunk is its last n tiles (k in [T-n, T)); chunk d is
+        // complete once rank d has produced them, every other rank's share
+        // of it coming from earlier steps.  Launch the earlier steps, then
+        // slices of the last step; reduce each slice's tiles on the
+        // auxiliary stream while the next slice computes.
+        const uint32_t W = (uint32_t)p->g.W, T = (uint32_t)p->g.T;
+        const uint32_t n = T / W;   // tiles per chunk (uniform)
+        const uint32_t k0 = T - n;
+        const uint32_t parts = n < (uint32_t)kSlices ? n : (uint32_t)kSlices;
+        e = gemm(0, W * k0, s);
+        for (uint32_t j = 0; j < parts && e == hipSuccess; ++j) {
+            const uint32_t q0 = k0 + (n * j) / parts, q1 = k0 + (n * (j + 1)) / parts;
+            e = gemm(W * q0, W * q1, s);
+            if (e == hipSuccess) e = hipEventRecord(p->slice_done[j], s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
+            if (e == hipSuccess) {
+                ReduceArgs rs = r;
+                rs.k_lo = q0;
+                rs.k_hi = q1;
+                e = launch_reduce(rs, p->d.dtype, p->aux);
+            }
+        }
+        if (e == hipSuccess) e = hipEventRecord(p->aux_done, p->aux);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, p->aux_done, 0);
+        return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
     }
-    if (do_reduce) {
-        ReduceArgs r;
-        r.g = p->g;
-        r.order = p->d.order;
-        r.groups = p->d.groups;
-        r.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
-        r.acquire = 0;   // the GEMM kernel ran before on this stream
-        r.units_per_tile = p->units_per_tile;
-        r.timeout_ticks = p->timeout_ticks;
-        r.staging = p->staging;
-        r.out = out;
-        r.flags = p->flags;
-        r.counters = p->counters;
-        r.err = p->err;
-        r.sub = p->sub;
-        r.sub_flags = p->sub_flags;
-        hipError_t e;
+
+    if (do_gemm) e = gemm(0, a.n_blocks, s);
+    if (e == hipSuccess && do_reduce) {
         if (p->d.materialize_sub) {
             ReduceArgs rs = r;
             rs.counters = p->sub_counters;
@@ -297,9 +364,8 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         } else {
             e = launch_reduce(r, p->d.dtype, s);
         }
-        if (e != hipSuccess) return GEMM_RS_ERR_HIP;
     }
-    return GEMM_RS_OK;
+    return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
 }
 
 int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {

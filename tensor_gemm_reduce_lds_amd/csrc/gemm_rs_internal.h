@@ -81,6 +81,8 @@ struct GemmArgs {
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
     int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
+    uint32_t b_offset;      // workgroup b = b_offset + blockIdx.x (launch slices)
+    uint32_t n_blocks;      // workgroups in this launch
 };
 
 struct ReduceArgs {
@@ -95,6 +97,10 @@ struct ReduceArgs {
     uint32_t *flags;         // [W][T]
     uint32_t *counters;      // [T] (flat) or [G][T] (sub stage)
     int32_t *err;            // {code, rank, tile, value}
+    // slice mode (k_hi > k_lo): units cover, for every chunk d, rank d's
+    // k-th tiles with k in [k_lo, k_hi) that lie in chunk d (rank d's own
+    // chunk, the last contribution to those tiles); otherwise all tiles
+    uint32_t k_lo, k_hi;
     // materialised two-level buffers (sub stage writes, final stage reads)
     float *sub;              // [W][G][Mc][N]
     uint32_t *sub_flags;     // [G][T*units_per_tile]

@@ -155,12 +155,35 @@ __device__ __forceinline__ void ordered_sum2(const float *S, const float *S2, in
     }
 }
 
+// Tile and slab of this workgroup.  Whole-grid mode: unit = t*U + slab.
+// Slice mode (k_hi > k_lo): unit = ((k - k_lo)*W + d)*U + slab names rank
+// d's k-th tile, taken only if it lies in chunk d; returns false otherwise.
+__device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32_t *slab) {
+    const TileGeom &g = a.g;
+    const uint32_t U = (uint32_t)a.units_per_tile, unit = blockIdx.x;
+    *slab = (int32_t)(unit % U);
+    if (a.k_hi <= a.k_lo) {
+        *t = (int32_t)(unit / U);
+        return true;
+    }
+    const uint32_t rest = unit / U, W = (uint32_t)g.W;
+    const int32_t d = (int32_t)(rest % W);
+    const uint32_t k = a.k_lo + rest / W;
+    const uint32_t n_d = (uint32_t)(chunk_first_tile_row(g, d + 1) - chunk_first_tile_row(g, d)) *
+                         (uint32_t)g.tiles_n;
+    if (k + n_d < (uint32_t)g.T) return false;   // rank d's k-th tile is not in chunk d
+    int32_t r;
+    tile_of_block(g, k * W + (uint32_t)d, &r, t);
+    return true;
+}
+
 // One-stage reduce: flags -> out.
 template <int WT, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const TileGeom &g = a.g;
     const int32_t U = a.units_per_tile;
-    const int32_t t = (int32_t)(blockIdx.x / U), slab = (int32_t)(blockIdx.x % U);
+    int32_t t, slab;
+    if (!unit_tile(a, &t, &slab)) return;
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t, a.acquire)) return;
@@ -292,7 +315,10 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
 
 template <bool BF>
 hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.g.T * a.units_per_tile));
+    const int64_t units = a.k_hi > a.k_lo
+                              ? (int64_t)(a.k_hi - a.k_lo) * a.g.W * a.units_per_tile
+                              : (int64_t)a.g.T * a.units_per_tile;
+    const dim3 grid((unsigned)units);
     switch (a.g.W) {
     case 1: hipLaunchKernelGGL((reduce_kernel<1, BF>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((reduce_kernel<2, BF>), grid, dim3(kThreads), 0, s, a); break;

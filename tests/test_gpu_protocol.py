@@ -158,3 +158,35 @@ def test_output_rounding_ties_w1():
     bits = _reduce_only(W, M, N, G.BF16, O.FLAT, 1, S)
     assert bits.ravel()[:4].tolist() == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
     assert np.array_equal(bits.ravel(), O.bf16_rne(S.ravel()))
+
+
+# ------------------------------------------------ overlapped reduce (slices)
+@pytest.mark.parametrize("name", ["llama8b", "ragged_2lvl", "decode",
+                                  "llama70b_small"])
+def test_overlapped_reduce_matches_serial_bits(name):
+    """The overlapped order (the GEMM's last step in slices, each slice's
+    tiles reduced on a second stream while the next slice computes) gives
+    the same bits as the serial order; decode has unequal chunks and takes
+    the serial path."""
+    import torch
+    if name == "llama70b_small":
+        w = I.with_shape(I.WORKLOADS["llama70b"], M=2048, N=1024, K=512)
+    else:
+        w = I.WORKLOADS[name]
+    say("overlap", name)
+    x, dev, plan = _setup(w)
+    with plan:
+        s = torch.cuda.current_stream()
+        ref, got = new_out(w), new_out(w)
+        run_checked(plan, dev, w, ref)
+        for _ in range(2):   # twice: flags must come back to 0 in between
+            plan.run(dev["A"], dev["B"], dev["C"], w.alpha, w.beta, got, s,
+                     G.RUN_ALL | G.OVERLAP_REDUCE)
+            rc, detail = plan.status(s)
+            assert rc == G.OK, detail
+            assert not flags(plan).any()
+            assert np.array_equal(out_bits(got), out_bits(ref))
+        plan.run(dev["A"], dev["B"], dev["C"], w.alpha, w.beta, got, s,
+                 G.RUN_ALL | G.OVERLAP_REDUCE | G.KEEP_FLAGS)
+        assert plan.status(s)[0] == G.OK
+        assert flags(plan).all()
