@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for cpu_baseline (0: skip)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the overlapped-reduce timing (profiling runs: every "
+                         "GEMM and reduce launch is then a full launch)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="MiB: run one plain device copy of this size first "
                          "(reference point for HBM byte counters)")
@@ -189,6 +192,22 @@ def main():
     if rc != G.OK:
         raise RuntimeError("timed run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
 
+    # the same steps with the reduce overlapped with the GEMM's last step
+    # (slices reduced on the plan's second stream); whole-step wall time only
+    ov_ms = None
+    if not args.no_overlap:
+        for _ in range(2):
+            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+        torch.cuda.synchronize()
+        ov_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        rc, detail = plan.status(stream)
+        if rc != G.OK:
+            raise RuntimeError("overlapped run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     step_ms = wall * 1e3 / args.steps
@@ -231,6 +250,8 @@ def main():
         "reduce_gbps": round(red_gbps, 1),
         "reduce_hbm_frac": round(red_gbps / PEAK_HBM_GBPS, 4),
         "reduce_algorithmic_bytes": red_bytes,
+        "ms_per_step_overlap": None if ov_ms is None else round(ov_ms, 4),
+        "value_overlap": None if ov_ms is None else round(flops / (ov_ms * 1e-3) / 1e12, 2),
     }
     plan.close()
     del A, B, C, out
