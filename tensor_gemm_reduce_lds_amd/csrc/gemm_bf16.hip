@@ -19,11 +19,14 @@
 //     16 lanes so that each lane gets 4 consecutive k of one column.
 //   * v_mfma_f32_32x32x16_bf16, fp32 accumulators.
 // Epilogue: alpha*acc, plus beta*C on rows whose chunk this rank owns,
-// stored as fp32 into the staging slot of each row's destination chunk;
-// then the tile's ready flag is released at agent scope (page "flux实现：
+// stored as fp32 into the staging slot of each row's destination chunk
+// (rows pass through LDS so that each store instruction writes whole
+// staging rows); then the tile's ready flag is published (page "flux实现：
 // sm80 gemm+rs", section "cutlass自定义epilogue–sm80": a compute node
 // alpha*acc + beta*C, a store node that scatters by destination, and a
 // per-tile flag).
+#include <type_traits>
+
 #include "gemm_rs_internal.h"
 
 namespace gemm_rs {
@@ -214,44 +217,102 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     }
 
     // ---- epilogue: D = alpha*acc (+ beta*C on owned rows), scatter ----
+    // The accumulators go out through LDS one 32-row stripe at a time so
+    // that every store instruction writes whole staging rows (64 lanes x
+    // 16 bytes = 1 KB contiguous for BN = 256): a store pattern of 32 rows x
+    // 32 bytes per instruction drains several times slower per CU.
     // Transposed 32x32 accumulator layout: lane holds output row (lane & 31)
     // of the block; registers 4q..4q+3 hold its columns 8q + 4*(lane/32)
-    // + 0..3.  Each lane therefore writes 16-byte runs of one staging row.
+    // + 0..3.
+    constexpr int EP_PITCH = BN * 4 + 16;          // bytes per staged row (padded)
+    constexpr int LPR = BN / 4;                    // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;                  // rows per store instruction
+    constexpr int SROWS = WGM * 32;                // rows per stripe
+    constexpr int ST_PER_WAVE = SROWS / (NW * RPI);
+    static_assert(SROWS * EP_PITCH <= STAGES * STAGE, "stripe fits in the stage buffers");
+    static_assert(ST_PER_WAVE * NW * RPI == SROWS, "stripe rows split evenly");
     const uint16_t *Cp = (const uint16_t *)a.C;
     const float alpha = a.alpha, beta = a.beta;
     const int h4 = 4 * (lane >> 5);
+    const int scol = (lane % LPR) * 4;              // this lane's 4 columns in a row
+    const int srow = lane / LPR;                    // row inside a store instruction
+    // C modes: 0 none, 1 bias row (ldc == 0: one 8-byte load per lane for
+    // the whole tile), 2 full matrix (the stripe's rows are loaded before
+    // its stores).  Each mode is separate code: a C load issued behind
+    // stores would have to wait for all of them (memory operations complete
+    // in order), so no load sits between two stores.
+    auto epilogue = [&](auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        uint2 cb_row = {0u, 0u};
+        if constexpr (MODE == 1) {
+            cb_row = *(const uint2 *)(Cp + col0 + scol);
+            asm volatile("" : "+v"(cb_row.x), "+v"(cb_row.y));   // wait here, once
+        }
+        __syncthreads();                            // every wave is done with the stages
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t row = row0 + wm * WM + i * 32 + (lane & 31);
-        if (row < g.M) {
-            const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
-            const bool own_c = a.has_c && d == r;
-            float *dst = a.staging +
-                         (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
-                         col0 + wn * WN + h4;
-            const uint16_t *crow = own_c ? Cp + row * a.ldc + col0 + wn * WN + h4 : nullptr;
+        for (int i = 0; i < FM; ++i) {
+            // stage block i of every wave: stripe wm holds tile rows
+            // wm*WM + i*32 .. +31 across all BN columns
+            lds_char *stripe = smem + wm * 32 * EP_PITCH;
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c = j * 32 + 8 * q;       // column offset in the wave tile
                     f32x4_t x;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
-                    if (own_c) {
-                        const uint2 cb = *(const uint2 *)(crow + c);
-                        x[0] += beta * __uint_as_float(cb.x << 16);
-                        x[1] += beta * __uint_as_float(cb.x & 0xffff0000u);
-                        x[2] += beta * __uint_as_float(cb.y << 16);
-                        x[3] += beta * __uint_as_float(cb.y & 0xffff0000u);
-                    }
-                    // a plain (write-back) store: the four 16-byte runs of a
-                    // 128-byte line come from four instructions and merge in
-                    // L2; a streaming hint here costs ~20%
-                    *(f32x4_t *)(dst + c) = x;
+                    *(__attribute__((address_space(3))) f32x4_t *)(
+                        stripe + (lane & 31) * EP_PITCH + (wn * WN + j * 32 + 8 * q + h4) * 4) = x;
                 }
+            uint2 cb_full[ST_PER_WAVE];
+            if constexpr (MODE == 2) {
+#pragma unroll
+                for (int k = 0; k < ST_PER_WAVE; ++k) {
+                    const int sr = (wave * ST_PER_WAVE + k) * RPI + srow;
+                    int64_t row = row0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+                    if (row > g.M - 1) row = g.M - 1;   // ragged M: a valid row
+                    cb_full[k] = *(const uint2 *)(Cp + row * a.ldc + col0 + scol);
+                }
+#pragma unroll
+                for (int k = 0; k < ST_PER_WAVE; ++k)   // one wait, before any store
+                    asm volatile("" : "+v"(cb_full[k].x), "+v"(cb_full[k].y));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < ST_PER_WAVE; ++k) {
+                const int sr = (wave * ST_PER_WAVE + k) * RPI + srow;   // row in the stripe set
+                const int64_t row = row0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+                f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
+                    smem + sr * EP_PITCH + scol * 4);
+                if (row < g.M) {
+                    const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
+                    if constexpr (MODE != 0) {
+                        const uint2 cb = MODE == 1 ? cb_row : cb_full[k];
+                        const float y0 = x[0] + beta * __uint_as_float(cb.x << 16);
+                        const float y1 = x[1] + beta * __uint_as_float(cb.x & 0xffff0000u);
+                        const float y2 = x[2] + beta * __uint_as_float(cb.y << 16);
+                        const float y3 = x[3] + beta * __uint_as_float(cb.y & 0xffff0000u);
+                        const bool own = d == r;    // C counts once: on its owner's rows
+                        x[0] = own ? y0 : x[0];
+                        x[1] = own ? y1 : x[1];
+                        x[2] = own ? y2 : x[2];
+                        x[3] = own ? y3 : x[3];
+                    }
+                    float *dst = a.staging +
+                                 (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
+                                 col0 + scol;
+                    // whole 128-byte lines from one instruction: a streaming
+                    // store keeps the 2 GB of staging from evicting the A/B
+                    // panels other tiles are still reading
+                    __builtin_nontemporal_store(x, (f32x4_t *)dst);
+                }
+            }
+            if (i + 1 < FM) __syncthreads();        // the stripe buffer is reused
         }
-    }
+    };
+    if (!a.has_c) epilogue(std::integral_constant<int, 0>{});
+    else if (a.ldc == 0) epilogue(std::integral_constant<int, 1>{});
+    else epilogue(std::integral_constant<int, 2>{});
 
     // ---- publish: all stores of this tile, then flag[r][t] = 1 ----
     // With a concurrent consumer the flag is an agent-scope release (the
