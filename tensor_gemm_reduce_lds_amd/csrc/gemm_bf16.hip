@@ -17,7 +17,8 @@
 //   * A operands come from ds_read_b128; B operands from two
 //     ds_read_b64_tr_b16 per MFMA, which transpose 4x16 bf16 blocks across
 //     16 lanes so that each lane gets 4 consecutive k of one column.
-//   * v_mfma_f32_32x32x16_bf16, fp32 accumulators.
+//   * v_mfma_f32_32x32x16_bf16, fp32 accumulators; the LDS reads of the
+//     next 16-deep slice are interleaved with the MFMAs of the current one.
 // Epilogue: alpha*acc, plus beta*C on rows whose chunk this rank owns,
 // stored as fp32 into the staging slot of each row's destination chunk
 // (rows pass through LDS so that each store instruction writes whole
@@ -173,31 +174,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    auto load_frags = [&](lds_char *S, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(S + a_off[i][ks]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][0]));
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][1]));
+            i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bfr[j] = __builtin_bit_cast(bf16x8_t, both);
+        }
+    };
+    // Operand fragments are double-buffered in registers: the LDS reads of
+    // the next 16-deep slice are interleaved one by one with the MFMAs of
+    // the current slice, so their latency hides behind the matrix pipe.
     auto compute = [&](int buf) {
         lds_char *S = smem + buf * STAGE;
+        bf16x8_t af[2][FM], bfr[2][FN];
+        load_frags(S, 0, af[0], bfr[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(S + a_off[i][ks]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][0]));
-                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][1]));
-                i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                bfr[j] = __builtin_bit_cast(bf16x8_t, both);
-            }
+            if (ks + 1 < BK / 16) load_frags(S, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     // operands swapped: the block comes out transposed, so a
                     // lane holds one output row and runs of 4 columns
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i],
-                                                                        acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        bfr[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
+            if (ks + 1 < BK / 16) {
+                // schedule: one LDS read (mask 0x100), one MFMA (0x008), ...
+#pragma unroll
+                for (int k = 0; k < FM + 2 * FN; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
