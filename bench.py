@@ -148,11 +148,12 @@ def main():
     A, B, C = up(x["A"]), up(x["B"]), up(x["C"])
     out = torch.empty((w.M, w.N), dtype=torch.int16 if w.dtype == "bf16" else torch.float32,
                       device=dev)
-    plan = G.Plan(M=w.M, N=w.N, K=w.K, W=w.W,
-                  dtype=G.BF16 if w.dtype == "bf16" else G.F32,
-                  tile_m=w.tile_m, tile_n=w.tile_n,
-                  order=G.ORDER_TWO_LEVEL if w.order == "two_level" else G.ORDER_FLAT,
-                  groups=w.groups, has_c=int(w.has_c), ldc=w.ldc)
+    plan_fields = dict(M=w.M, N=w.N, K=w.K, W=w.W,
+                       dtype=G.BF16 if w.dtype == "bf16" else G.F32,
+                       tile_m=w.tile_m, tile_n=w.tile_n,
+                       order=G.ORDER_TWO_LEVEL if w.order == "two_level" else G.ORDER_FLAT,
+                       groups=w.groups, has_c=int(w.has_c), ldc=w.ldc)
+    plan = G.Plan(**plan_fields)
     stream = torch.cuda.current_stream()
 
     if args.copy_calibration > 0:
@@ -192,21 +193,29 @@ def main():
     if rc != G.OK:
         raise RuntimeError("timed run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
 
-    # the same steps with the reduce overlapped with the GEMM's last step
-    # (slices reduced on the plan's second stream); whole-step wall time only
-    ov_ms = None
-    if not args.no_overlap:
+    # the same steps with the reduce overlapped with the GEMM (slices reduced
+    # on the plan's second stream); whole-step wall time only.  Remote-first
+    # order: the reduce overlaps the last step's slices; identity order (a
+    # second plan): chunk c's reduce overlaps the GEMM of chunk c+1.
+    def overlapped_ms(p):
         for _ in range(2):
-            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+            p.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(args.steps):
-            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+            p.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
         torch.cuda.synchronize()
-        ov_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-        rc, detail = plan.status(stream)
+        ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        rc, detail = p.status(stream)
         if rc != G.OK:
             raise RuntimeError("overlapped run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+        return ms
+
+    ov_ms = ov_id_ms = None
+    if not args.no_overlap:
+        ov_ms = overlapped_ms(plan)
+        with G.Plan(**dict(plan_fields, swizzle=G.SWIZZLE_IDENTITY)) as plan_id:
+            ov_id_ms = overlapped_ms(plan_id)
 
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -252,6 +261,9 @@ def main():
         "reduce_algorithmic_bytes": red_bytes,
         "ms_per_step_overlap": None if ov_ms is None else round(ov_ms, 4),
         "value_overlap": None if ov_ms is None else round(flops / (ov_ms * 1e-3) / 1e12, 2),
+        "ms_per_step_overlap_identity": None if ov_id_ms is None else round(ov_id_ms, 4),
+        "value_overlap_identity": (None if ov_id_ms is None
+                                   else round(flops / (ov_id_ms * 1e-3) / 1e12, 2)),
     }
     plan.close()
     del A, B, C, out

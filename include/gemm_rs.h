@@ -72,7 +72,7 @@ extern "C" {
 #define GEMM_RS_KEEP_FLAGS  4u /* debug: the reduce leaves flags at 1       */
 #define GEMM_RS_TRACE_TILES 8u /* debug: GEMM records trace[b] = tile of WG b */
 #define GEMM_RS_OVERLAP_REDUCE 16u /* with RUN_GEMM|RUN_REDUCE: overlap the reduce
-                                      with the GEMM's last step (see gemm_rs_run) */
+                                      with the GEMM (see gemm_rs_run) */
 #define GEMM_RS_RUN_ALL     (GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE)
 
 /*
@@ -161,14 +161,18 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
  *        rows [d*M/W, (d+1)*M/W) are rank d's chunk
  *   run_flags  GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE, plus the debug bits,
  *              plus GEMM_RS_OVERLAP_REDUCE
- * GEMM_RS_OVERLAP_REDUCE (remote-first tile order, flat or register
- * two-level reduce, both RUN bits; otherwise ignored): chunk d is complete
- * only when rank d has computed its own chunk, which the remote-first order
- * puts in every rank's last step.  The GEMM is then launched as the earlier
- * steps plus four slices of the last step; after each slice an auxiliary
- * stream owned by the plan reduces exactly the tiles that slice completed,
- * concurrently with the next slice, and `stream` waits for the auxiliary
- * stream at the end.  Results are bit-identical to the serial order.
+ * GEMM_RS_OVERLAP_REDUCE (both RUN bits, flat or register two-level
+ * reduce, every chunk owning the same number of tile rows, remote-first or
+ * identity tile order; otherwise ignored): the GEMM is launched in slices
+ * of the tile order and, after each slice, an auxiliary stream owned by the
+ * plan reduces exactly the tiles that slice completed, concurrently with
+ * the next slice; `stream` waits for the auxiliary stream at the end.
+ * Remote-first order: chunk d is complete only when rank d has computed its
+ * own chunk, which that order puts in every rank's last step, so the slices
+ * are the earlier steps plus four slices of the last step.  Identity order:
+ * every rank computes chunk c in the same steps, so chunk c is complete
+ * after them and its reduce overlaps the GEMM of the following chunks (up
+ * to eight slices).  Results are bit-identical to the serial order.
  * The caller owns A, B, C, out and the stream, and keeps them alive until
  * the stream's work is done.  Calls on one stream are ordered; one plan
  * must not run on two streams at once.  A device-side flag-wait timeout or

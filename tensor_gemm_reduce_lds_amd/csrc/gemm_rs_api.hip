@@ -11,11 +11,14 @@
 
 using namespace gemm_rs;
 
-// slices of the last tile-order step in the overlapped-reduce path
+// overlapped reduce: slices of the last tile-order step (remote-first
+// order), and at most this many chunk groups (identity order)
 #ifndef GEMM_RS_SLICES
 #define GEMM_RS_SLICES 4
 #endif
 constexpr int kSlices = GEMM_RS_SLICES;
+constexpr int kChunkSlices = 8;
+constexpr int kEvents = kSlices > kChunkSlices ? kSlices : kChunkSlices;
 
 struct gemm_rs_plan_s {
     gemm_rs_desc_t d;        // resolved (tiles, group_m, timeout filled in)
@@ -35,7 +38,7 @@ struct gemm_rs_plan_s {
         sub_flags_bytes, trace_bytes;
     // overlapped reduce: an auxiliary stream (default priority) and events
     hipStream_t aux;
-    hipEvent_t slice_done[kSlices];
+    hipEvent_t slice_done[kEvents];
     hipEvent_t aux_done;
     bool uniform_chunks;     // every chunk owns the same number of tiles
 };
@@ -117,7 +120,7 @@ void free_plan(gemm_rs_plan_s *p) {
     hipFree(p->sub_flags);
     hipFree(p->err);
     hipFree(p->trace);
-    for (int i = 0; i < kSlices; ++i)
+    for (int i = 0; i < kEvents; ++i)
         if (p->slice_done[i]) hipEventDestroy(p->slice_done[i]);
     if (p->aux_done) hipEventDestroy(p->aux_done);
     if (p->aux) hipStreamDestroy(p->aux);
@@ -212,7 +215,7 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
             e = hipMalloc(&p->sub_counters, p->counters_bytes * d.groups);
     }
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
-    for (int i = 0; i < kSlices && e == hipSuccess; ++i)
+    for (int i = 0; i < kEvents && e == hipSuccess; ++i)
         e = hipEventCreateWithFlags(&p->slice_done[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->aux_done, hipEventDisableTiming);
     {
@@ -320,34 +323,52 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     r.err = p->err;
     r.sub = p->sub;
     r.sub_flags = p->sub_flags;
+    r.slice_kind = kSliceAll;
     r.k_lo = r.k_hi = 0;
 
     const bool overlap = (run_flags & GEMM_RS_OVERLAP_REDUCE) && do_gemm && do_reduce &&
-                         p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST &&
-                         !p->d.materialize_sub && p->uniform_chunks;
+                         !p->d.materialize_sub && p->uniform_chunks &&
+                         (p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST ||
+                          p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY);
     hipError_t e = hipSuccess;
     if (overlap) {
-        // rank d's own chunk is its last n tiles (k in [T-n, T)); chunk d is
-        // complete once rank d has produced them, every other rank's share
-        // of it coming from earlier steps.  Launch the earlier steps, then
-        // slices of the last step; reduce each slice's tiles on the
-        // auxiliary stream while the next slice computes.
         const uint32_t W = (uint32_t)p->g.W, T = (uint32_t)p->g.T;
         const uint32_t n = T / W;   // tiles per chunk (uniform)
-        const uint32_t k0 = T - n;
-        const uint32_t parts = n < (uint32_t)kSlices ? n : (uint32_t)kSlices;
-        e = gemm(0, W * k0, s);
-        for (uint32_t j = 0; j < parts && e == hipSuccess; ++j) {
-            const uint32_t q0 = k0 + (n * j) / parts, q1 = k0 + (n * (j + 1)) / parts;
-            e = gemm(W * q0, W * q1, s);
-            if (e == hipSuccess) e = hipEventRecord(p->slice_done[j], s);
-            if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
-            if (e == hipSuccess) {
+        // GEMM steps [q0, q1) of every rank, then the reduce of the tiles
+        // they completed on the auxiliary stream, concurrent with the next
+        // GEMM slice
+        auto slice = [&](int j, uint32_t q0, uint32_t q1, int kind) {
+            hipError_t x = gemm(W * q0, W * q1, s);
+            if (x == hipSuccess) x = hipEventRecord(p->slice_done[j], s);
+            if (x == hipSuccess) x = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
+            if (x == hipSuccess) {
                 ReduceArgs rs = r;
+                rs.slice_kind = kind;
                 rs.k_lo = q0;
                 rs.k_hi = q1;
-                e = launch_reduce(rs, p->d.dtype, p->aux);
+                x = launch_reduce(rs, p->d.dtype, p->aux);
             }
+            return x;
+        };
+        if (p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST) {
+            // rank d's own chunk is its last n tiles (k in [T-n, T)); chunk
+            // d is complete once rank d has produced them, every other
+            // rank's share of it coming from earlier steps: the earlier
+            // steps, then slices of the last step
+            const uint32_t k0 = T - n;
+            const uint32_t parts = n < (uint32_t)kSlices ? n : (uint32_t)kSlices;
+            e = gemm(0, W * k0, s);
+            for (uint32_t j = 0; j < parts && e == hipSuccess; ++j)
+                e = slice((int)j, k0 + (n * j) / parts, k0 + (n * (j + 1)) / parts,
+                          kSliceLastStep);
+        } else {
+            // identity order: every rank computes chunk c in steps
+            // [c*n, (c+1)*n), so chunk c is complete after them; chunks are
+            // grouped into at most kChunkSlices slices
+            const uint32_t parts = W < (uint32_t)kChunkSlices ? W : (uint32_t)kChunkSlices;
+            for (uint32_t j = 0; j < parts && e == hipSuccess; ++j)
+                e = slice((int)j, n * ((W * j) / parts), n * ((W * (j + 1)) / parts),
+                          kSliceSteps);
         }
         if (e == hipSuccess) e = hipEventRecord(p->aux_done, p->aux);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, p->aux_done, 0);

@@ -85,6 +85,8 @@ struct GemmArgs {
     uint32_t n_blocks;      // workgroups in this launch
 };
 
+enum { kSliceAll = 0, kSliceLastStep = 1, kSliceSteps = 2 };
+
 struct ReduceArgs {
     TileGeom g;
     int32_t order, groups;   // groups == 1 for flat
@@ -97,9 +99,14 @@ struct ReduceArgs {
     uint32_t *flags;         // [W][T]
     uint32_t *counters;      // [T] (flat) or [G][T] (sub stage)
     int32_t *err;            // {code, rank, tile, value}
-    // slice mode (k_hi > k_lo): units cover, for every chunk d, rank d's
-    // k-th tiles with k in [k_lo, k_hi) that lie in chunk d (rank d's own
-    // chunk, the last contribution to those tiles); otherwise all tiles
+    // which tiles the grid covers (steps k of the tile order, [k_lo, k_hi)):
+    //   kSliceAll      every tile
+    //   kSliceLastStep for every chunk d, rank d's k-th tiles that lie in
+    //                  chunk d (remote-first order: rank d's own chunk, the
+    //                  last contribution to those tiles)
+    //   kSliceSteps    the k-th tile of the common order (identity order:
+    //                  every rank computes tile seq[k] in step k)
+    int32_t slice_kind;
     uint32_t k_lo, k_hi;
     // materialised two-level buffers (sub stage writes, final stage reads)
     float *sub;              // [W][G][Mc][N]

@@ -159,24 +159,30 @@ __device__ __forceinline__ void ordered_sum2(const float *S, const float *S2, in
     }
 }
 
-// Tile and slab of this workgroup.  Whole-grid mode: unit = t*U + slab.
-// Slice mode (k_hi > k_lo): unit = ((k - k_lo)*W + d)*U + slab names rank
-// d's k-th tile, taken only if it lies in chunk d; returns false otherwise.
+// Tile and slab of this workgroup.  kSliceAll: unit = t*U + slab.
+// kSliceLastStep: unit = ((k - k_lo)*W + d)*U + slab names rank d's k-th
+// tile, taken only if it lies in chunk d; returns false otherwise.
+// kSliceSteps: unit = (k - k_lo)*U + slab names the k-th tile of the order
+// every rank shares (rank 0's k-th tile).
 __device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32_t *slab) {
     const TileGeom &g = a.g;
     const uint32_t U = (uint32_t)a.units_per_tile, unit = blockIdx.x;
     *slab = (int32_t)(unit % U);
-    if (a.k_hi <= a.k_lo) {
-        *t = (int32_t)(unit / U);
+    const uint32_t rest = unit / U, W = (uint32_t)g.W;
+    int32_t r;
+    if (a.slice_kind == kSliceAll) {
+        *t = (int32_t)rest;
         return true;
     }
-    const uint32_t rest = unit / U, W = (uint32_t)g.W;
+    if (a.slice_kind == kSliceSteps) {
+        tile_of_block(g, (a.k_lo + rest) * W, &r, t);
+        return true;
+    }
     const int32_t d = (int32_t)(rest % W);
     const uint32_t k = a.k_lo + rest / W;
     const uint32_t n_d = (uint32_t)(chunk_first_tile_row(g, d + 1) - chunk_first_tile_row(g, d)) *
                          (uint32_t)g.tiles_n;
     if (k + n_d < (uint32_t)g.T) return false;   // rank d's k-th tile is not in chunk d
-    int32_t r;
     tile_of_block(g, k * W + (uint32_t)d, &r, t);
     return true;
 }
@@ -319,9 +325,11 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
 
 template <bool BF>
 hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
-    const int64_t units = a.k_hi > a.k_lo
-                              ? (int64_t)(a.k_hi - a.k_lo) * a.g.W * a.units_per_tile
-                              : (int64_t)a.g.T * a.units_per_tile;
+    const int64_t units =
+        a.slice_kind == kSliceLastStep ? (int64_t)(a.k_hi - a.k_lo) * a.g.W * a.units_per_tile
+        : a.slice_kind == kSliceSteps  ? (int64_t)(a.k_hi - a.k_lo) * a.units_per_tile
+                                       : (int64_t)a.g.T * a.units_per_tile;
+    if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)units);
     switch (a.g.W) {
     case 1: hipLaunchKernelGGL((reduce_kernel<1, BF>), grid, dim3(kThreads), 0, s, a); break;

@@ -161,24 +161,31 @@ def test_output_rounding_ties_w1():
 
 
 # ------------------------------------------------ overlapped reduce (slices)
+@pytest.mark.parametrize("swizzle", [G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_IDENTITY])
 @pytest.mark.parametrize("name", ["llama8b", "ragged_2lvl", "decode",
                                   "llama70b_small"])
-def test_overlapped_reduce_matches_serial_bits(name):
-    """The overlapped order (the GEMM's last step in slices, each slice's
-    tiles reduced on a second stream while the next slice computes) gives
-    the same bits as the serial order; decode has unequal chunks and takes
-    the serial path."""
+def test_overlapped_reduce_matches_serial_bits(name, swizzle):
+    """The overlapped order (the GEMM in slices, each slice's completed
+    tiles reduced on a second stream while the next slice computes: the
+    last step's slices for the remote-first order, chunk by chunk for the
+    identity order) gives the same bits as the serial remote-first order;
+    decode has unequal chunks and takes the serial path."""
     import torch
     if name == "llama70b_small":
         w = I.with_shape(I.WORKLOADS["llama70b"], M=2048, N=1024, K=512)
     else:
         w = I.WORKLOADS[name]
-    say("overlap", name)
-    x, dev, plan = _setup(w)
+    say("overlap", name, "swizzle", swizzle)
+    x, dev, plan = _setup(w, swizzle=swizzle)
     with plan:
         s = torch.cuda.current_stream()
         ref, got = new_out(w), new_out(w)
-        run_checked(plan, dev, w, ref)
+        if swizzle == G.SWIZZLE_REMOTE_FIRST:
+            run_checked(plan, dev, w, ref)
+        else:
+            # the tile order does not change any element's arithmetic
+            with G.Plan(**desc_fields(w)) as plan_rf:
+                run_checked(plan_rf, dev, w, ref)
         for _ in range(2):   # twice: flags must come back to 0 in between
             plan.run(dev["A"], dev["B"], dev["C"], w.alpha, w.beta, got, s,
                      G.RUN_ALL | G.OVERLAP_REDUCE)
