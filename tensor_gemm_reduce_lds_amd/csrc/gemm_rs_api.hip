@@ -112,19 +112,20 @@ void free_plan(gemm_rs_plan_s *p) {
     bool switched = false;
     if (hipGetDevice(&cur) == hipSuccess && cur != p->device)
         switched = hipSetDevice(p->device) == hipSuccess;
-    hipFree(p->staging);
-    hipFree(p->flags);
-    hipFree(p->counters);
-    hipFree(p->sub_counters);
-    hipFree(p->sub);
-    hipFree(p->sub_flags);
-    hipFree(p->err);
-    hipFree(p->trace);
+    // teardown is best effort: a failure here leaves nothing to undo
+    (void)hipFree(p->staging);
+    (void)hipFree(p->flags);
+    (void)hipFree(p->counters);
+    (void)hipFree(p->sub_counters);
+    (void)hipFree(p->sub);
+    (void)hipFree(p->sub_flags);
+    (void)hipFree(p->err);
+    (void)hipFree(p->trace);
     for (int i = 0; i < kEvents; ++i)
-        if (p->slice_done[i]) hipEventDestroy(p->slice_done[i]);
-    if (p->aux_done) hipEventDestroy(p->aux_done);
-    if (p->aux) hipStreamDestroy(p->aux);
-    if (switched) hipSetDevice(cur);
+        if (p->slice_done[i]) (void)hipEventDestroy(p->slice_done[i]);
+    if (p->aux_done) (void)hipEventDestroy(p->aux_done);
+    if (p->aux) (void)hipStreamDestroy(p->aux);
+    if (switched) (void)hipSetDevice(cur);
     free(p);
 }
 
