@@ -65,6 +65,10 @@ extern "C" {
 #define GEMM_RS_SWIZZLE_REMOTE_FIRST 0 /* dest(r,s) = (r+1+s) mod W (default) */
 #define GEMM_RS_SWIZZLE_SELF_FIRST   1 /* dest(r,s) = (r+s) mod W             */
 #define GEMM_RS_SWIZZLE_IDENTITY     2 /* dest(r,s) = s (no swizzle)          */
+#define GEMM_RS_SWIZZLE_TILE_INTERLEAVED 3 /* dest(r,s) = (r+1+s) mod W, visited
+                                              one tile at a time: rank r's k-th
+                                              tile goes to dest(r, k mod W)
+                                              while every chunk has tiles left */
 
 /* ---- run flags ---------------------------------------------------------- */
 #define GEMM_RS_RUN_GEMM    1u /* GEMM + epilogue + flag publish            */

@@ -35,7 +35,7 @@ import numpy as np
 OK, INVALID_ARG, UNSUPPORTED, HIP_ERROR, TIMEOUT, PROTOCOL = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
 FLAT, TWO_LEVEL = 0, 1
-REMOTE_FIRST, SELF_FIRST, IDENTITY = 0, 1, 2
+REMOTE_FIRST, SELF_FIRST, IDENTITY, TILE_INTERLEAVED = 0, 1, 2, 3
 RUN_GEMM, RUN_REDUCE, KEEP_FLAGS, TRACE_TILES = 1, 2, 4, 8
 MAX_W = 64
 K_STEP = 64
@@ -82,7 +82,7 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
         return INVALID_ARG
     if order == TWO_LEVEL and (groups < 1 or W % groups != 0):
         return INVALID_ARG
-    if swizzle not in (REMOTE_FIRST, SELF_FIRST, IDENTITY):
+    if swizzle not in (REMOTE_FIRST, SELF_FIRST, IDENTITY, TILE_INTERLEAVED):
         return INVALID_ARG
     if has_c not in (0, 1) or ldc < 0 or (has_c and ldc != 0 and ldc < N):
         return INVALID_ARG
@@ -179,8 +179,10 @@ class Geometry:
         section 4.1 (rank 1 writes chunks 1..7 then 0, rank 0 writes 0..7).
         IDENTITY: every rank in the same order 0..W-1 (the contention case
         the swizzle exists to avoid).
+        TILE_INTERLEAVED: the remote-first rotation, visited one tile at a
+        time (see ``seq``).
         """
-        if self.swizzle == REMOTE_FIRST:
+        if self.swizzle in (REMOTE_FIRST, TILE_INTERLEAVED):
             return (r + 1 + s) % self.W
         if self.swizzle == SELF_FIRST:
             return (r + s) % self.W
@@ -189,21 +191,40 @@ class Geometry:
     def chunk_tile_rows(self, d: int) -> List[int]:
         return [tm for tm in range(self.tiles_m) if self.owner(tm) == d]
 
+    def chunk_tiles(self, d: int) -> List[int]:
+        """Tiles of chunk d in their within-chunk order: sorted by
+        (tile-row group, tile column, tile row) with groups of ``group_m``
+        tile-rows counted from the chunk's first tile-row.  Tile id
+        t = tm * tiles_n + tn."""
+        rows = self.chunk_tile_rows(d)
+        if not rows:
+            return []
+        tm0 = rows[0]
+        tiles = [(tm, tn) for tm in rows for tn in range(self.tiles_n)]
+        tiles.sort(key=lambda x: ((x[0] - tm0) // self.g, x[1], x[0]))
+        return [tm * self.tiles_n + tn for tm, tn in tiles]
+
     def seq(self, r: int) -> List[int]:
-        """Tile order of rank r: chunk by chunk in dest order; inside a
-        chunk, tiles sorted by (tile-row group, tile column, tile row) with
-        groups of ``group_m`` tile-rows counted from the chunk's first
-        tile-row.  Tile id t = tm * tiles_n + tn."""
+        """Tile order of rank r.
+
+        Chunk-major orders (REMOTE_FIRST, SELF_FIRST, IDENTITY): chunk by
+        chunk in dest order, each chunk's tiles in their within-chunk order.
+        TILE_INTERLEAVED (a reading of the tile-interleaved variant of the
+        remote-first order: every destination in flight at once instead of
+        one chunk per step): rank r visits the destinations dest(r, 0..W-1)
+        in turn and takes the next tile of each on every visit; a chunk
+        whose tiles are used up is skipped."""
+        if self.swizzle != TILE_INTERLEAVED:
+            out = []
+            for s in range(self.W):
+                out.extend(self.chunk_tiles(self.dest(r, s)))
+            return out
+        lists = [self.chunk_tiles(self.dest(r, s)) for s in range(self.W)]
         out = []
-        for s in range(self.W):
-            d = self.dest(r, s)
-            rows = self.chunk_tile_rows(d)
-            if not rows:
-                continue
-            tm0 = rows[0]
-            tiles = [(tm, tn) for tm in rows for tn in range(self.tiles_n)]
-            tiles.sort(key=lambda x: ((x[0] - tm0) // self.g, x[1], x[0]))
-            out.extend(tm * self.tiles_n + tn for tm, tn in tiles)
+        for j in range(max(len(x) for x in lists)):
+            for s in range(self.W):
+                if j < len(lists[s]):
+                    out.append(lists[s][j])
         return out
 
     def seq_table(self) -> np.ndarray:

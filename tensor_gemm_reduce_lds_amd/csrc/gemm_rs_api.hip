@@ -83,7 +83,8 @@ int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
         return GEMM_RS_ERR_INVALID_ARG;
     if (d.swizzle != GEMM_RS_SWIZZLE_REMOTE_FIRST &&
         d.swizzle != GEMM_RS_SWIZZLE_SELF_FIRST &&
-        d.swizzle != GEMM_RS_SWIZZLE_IDENTITY)
+        d.swizzle != GEMM_RS_SWIZZLE_IDENTITY &&
+        d.swizzle != GEMM_RS_SWIZZLE_TILE_INTERLEAVED)
         return GEMM_RS_ERR_INVALID_ARG;
     if ((d.has_c != 0 && d.has_c != 1) || d.ldc < 0 ||
         (d.has_c && d.ldc != 0 && d.ldc < d.N))

@@ -32,41 +32,96 @@ __host__ __device__ inline int32_t chunk_first_tile_row(const TileGeom &g, int32
 }
 
 __host__ __device__ inline int32_t dest_chunk(const TileGeom &g, int32_t r, int32_t s) {
-    if (g.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST) return (r + 1 + s) % g.W;
+    if (g.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST ||
+        g.swizzle == GEMM_RS_SWIZZLE_TILE_INTERLEAVED)
+        return (r + 1 + s) % g.W;
     if (g.swizzle == GEMM_RS_SWIZZLE_SELF_FIRST) return (r + s) % g.W;
     return s;
 }
 
+// Tiles owned by chunk d: its tile-rows [first(d), first(d+1)) x tiles_n.
+__host__ __device__ inline uint32_t chunk_tiles(const TileGeom &g, int32_t d) {
+    return (uint32_t)(chunk_first_tile_row(g, d + 1) - chunk_first_tile_row(g, d)) *
+           (uint32_t)g.tiles_n;
+}
+
+// The j-th tile of chunk d in its within-chunk order: tile-rows in groups
+// of group_m, a group walked column by column, rows inside a column.
+__host__ __device__ inline int32_t tile_in_chunk(const TileGeom &g, int32_t d, uint32_t j) {
+    const uint32_t lo = (uint32_t)chunk_first_tile_row(g, d);
+    const uint32_t rows = (uint32_t)chunk_first_tile_row(g, d + 1) - lo;
+    const uint32_t gm = (uint32_t)g.group_m, tn_count = (uint32_t)g.tiles_n;
+    const uint32_t per_group = gm * tn_count;
+    const uint32_t grp = j / per_group;
+    const uint32_t q = j - grp * per_group;
+    const uint32_t left = rows - grp * gm;
+    const uint32_t grp_rows = left < gm ? left : gm;
+    const uint32_t tn = q / grp_rows;
+    const uint32_t tm = lo + grp * gm + (q - tn * grp_rows);
+    return (int32_t)(tm * tn_count + tn);
+}
+
 // Tile of workgroup b: rank r = b % W takes its k-th tile, k = b / W.
-// Rank r walks destination chunks dest(r, 0..W-1); chunk d holds the
-// tile-rows [first(d), first(d+1)); inside a chunk, tile-rows are grouped
-// by group_m and a group is walked column by column, rows inside a column.
+// Chunk-major orders: rank r walks destination chunks dest(r, 0..W-1), each
+// chunk's tiles in their within-chunk order.  Tile-interleaved order: rank
+// r visits dest(r, 0..W-1) in turn and takes the next tile of each on every
+// visit (visit j takes a chunk's j-th tile), skipping used-up chunks.
 __host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
                                               int32_t *rank, int32_t *tile) {
-    const uint32_t W = (uint32_t)g.W, tn_count = (uint32_t)g.tiles_n;
+    const uint32_t W = (uint32_t)g.W;
     const uint32_t r = b % W;
     uint32_t k = b / W;
-    uint32_t tm = 0, tn = 0;
+    *rank = (int32_t)r;
+    if (g.swizzle == GEMM_RS_SWIZZLE_TILE_INTERLEAVED) {
+        uint32_t n_min = 0xffffffffu, n_max = 0;
+        for (int32_t d = 0; d < g.W; ++d) {
+            const uint32_t n = chunk_tiles(g, d);
+            n_min = n < n_min ? n : n_min;
+            n_max = n > n_max ? n : n_max;
+        }
+        uint32_t j, s;
+        if (k < W * n_min) {           // every chunk still has tiles
+            j = k / W;
+            s = k - j * W;
+        } else {
+            // visits before round j: cb(j) = sum_d min(n_d, j); find the
+            // last round j with cb(j) <= k (cb(n_max) = T > k)
+            auto cb = [&](uint32_t jj) {
+                uint32_t c = 0;
+                for (int32_t d = 0; d < g.W; ++d) {
+                    const uint32_t n = chunk_tiles(g, d);
+                    c += n < jj ? n : jj;
+                }
+                return c;
+            };
+            uint32_t lo = n_min, hi = n_max - 1;
+            while (lo < hi) {
+                const uint32_t mid = lo + (hi - lo + 1) / 2;
+                if (cb(mid) <= k) lo = mid;
+                else hi = mid - 1;
+            }
+            j = lo;
+            uint32_t q = k - cb(j);    // the q-th chunk (in visit order) still open
+            for (s = 0; s < W; ++s) {
+                if (chunk_tiles(g, dest_chunk(g, (int32_t)r, (int32_t)s)) > j) {
+                    if (q == 0) break;
+                    --q;
+                }
+            }
+        }
+        *tile = tile_in_chunk(g, dest_chunk(g, (int32_t)r, (int32_t)s), j);
+        return;
+    }
     for (int32_t s = 0; s < g.W; ++s) {
         const int32_t d = dest_chunk(g, (int32_t)r, s);
-        const uint32_t lo = (uint32_t)chunk_first_tile_row(g, d);
-        const uint32_t rows = (uint32_t)chunk_first_tile_row(g, d + 1) - lo;
-        const uint32_t n = rows * tn_count;
+        const uint32_t n = chunk_tiles(g, d);
         if (k < n) {
-            const uint32_t gm = (uint32_t)g.group_m;
-            const uint32_t per_group = gm * tn_count;
-            const uint32_t grp = k / per_group;
-            const uint32_t q = k - grp * per_group;
-            const uint32_t left = rows - grp * gm;
-            const uint32_t grp_rows = left < gm ? left : gm;
-            tn = q / grp_rows;
-            tm = lo + grp * gm + (q - tn * grp_rows);
-            break;
+            *tile = tile_in_chunk(g, d, k);
+            return;
         }
         k -= n;
     }
-    *rank = (int32_t)r;
-    *tile = (int32_t)(tm * tn_count + tn);
+    *tile = 0;   // unreachable for b < W*T
 }
 
 struct GemmArgs {

@@ -26,7 +26,7 @@ ERR_PROTOCOL = -5
 
 BF16, F32 = 0, 1
 ORDER_FLAT, ORDER_TWO_LEVEL = 0, 1
-SWIZZLE_REMOTE_FIRST, SWIZZLE_SELF_FIRST, SWIZZLE_IDENTITY = 0, 1, 2
+SWIZZLE_REMOTE_FIRST, SWIZZLE_SELF_FIRST, SWIZZLE_IDENTITY, SWIZZLE_TILE_INTERLEAVED = 0, 1, 2, 3
 RUN_GEMM, RUN_REDUCE, KEEP_FLAGS, TRACE_TILES, OVERLAP_REDUCE = 1, 2, 4, 8, 16
 RUN_ALL = RUN_GEMM | RUN_REDUCE
 

@@ -70,7 +70,8 @@ def test_strerror_and_null_handles():
 
 BAD = [
     dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=0), dict(dtype=7),
-    dict(order=2), dict(order=1, groups=3), dict(order=1, groups=0), dict(swizzle=3),
+    dict(order=2), dict(order=1, groups=3), dict(order=1, groups=0), dict(swizzle=4),
+    dict(swizzle=-1),
     dict(has_c=1, ldc=100), dict(has_c=2), dict(ldc=-8), dict(materialize_sub=1),
     dict(materialize_sub=2, order=1, groups=2), dict(group_m=-1), dict(tile_m=-64),
     dict(tile_m=128, tile_n=64), dict(tile_m=32, tile_n=32), dict(N=1000),

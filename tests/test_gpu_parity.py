@@ -72,6 +72,8 @@ def test_materialised_two_level_matches_register_two_level():
 
 @pytest.mark.parametrize("over", [dict(swizzle=G.SWIZZLE_SELF_FIRST),
                                   dict(swizzle=G.SWIZZLE_IDENTITY),
+                                  dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED),
+                                  dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, group_m=3),
                                   dict(group_m=2), dict(group_m=3)])
 def test_tile_order_does_not_change_bits(over):
     w = dict(SMALL)["bf16_256x256_ragged"]
@@ -86,6 +88,12 @@ ORDER_CASES = [
     ("ragged_2lvl", {}), ("llama70b", dict(group_m=4)),
     ("ragged_2lvl", dict(group_m=3)), ("llama8b", dict(swizzle=G.SWIZZLE_SELF_FIRST)),
     ("llama8b", dict(swizzle=G.SWIZZLE_IDENTITY)),
+    # tile-interleaved: equal chunks, ragged chunks (straddling tiles, the
+    # binary-searched tail), and decode (chunks without tiles)
+    ("llama70b", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED)),
+    ("ragged_2lvl", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, group_m=3)),
+    ("decode", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED)),
+    ("tiny_f32", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED)),
 ]
 
 
@@ -99,12 +107,13 @@ def test_tile_order_matches_oracle_bit_exact(name, over):
     assert np.array_equal(got, want)
 
 
-def test_gemm_trace_matches_oracle():
+@pytest.mark.parametrize("swizzle", [G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_TILE_INTERLEAVED])
+def test_gemm_trace_matches_oracle(swizzle):
     w = dict(SMALL)["bf16_256x256_ragged"]
     x = I.make_inputs(w)
     dev = to_device(x, w)
-    say("gemm trace", w.name)
-    with G.Plan(**desc_fields(w, group_m=2)) as plan:
+    say("gemm trace", w.name, "swizzle", swizzle)
+    with G.Plan(**desc_fields(w, group_m=2, swizzle=swizzle)) as plan:
         out = new_out(w)
         run_checked(plan, dev, w, out, G.RUN_ALL | G.TRACE_TILES)
         tr = d2h(plan.info.trace, w.W * plan.info.T * 4, np.int32)
@@ -250,8 +259,10 @@ def test_edge_full_parity(name, w, over):
 
 def test_edge_tile_orders_bit_exact():
     for name, w, over in EDGE:
-        with G.Plan(**desc_fields(w, **over)) as plan:
-            assert np.array_equal(plan.tile_order(), geometry(w, plan).trace()), name
+        for swz in (G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_TILE_INTERLEAVED):
+            with G.Plan(**desc_fields(w, **dict(over, swizzle=swz))) as plan:
+                assert np.array_equal(plan.tile_order(), geometry(w, plan).trace()), \
+                    (name, swz)
 
 
 @pytest.mark.parametrize("tile", [(256, 128), (128, 128)])

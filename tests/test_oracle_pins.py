@@ -294,6 +294,46 @@ def test_self_first_matches_page_example():
         assert [R.dest(r, s) for s in range(8)] == want[1:] + want[:1]
 
 
+def test_tile_interleaved_hand_examples():
+    # W=2, two chunks of one tile-row each, 2 tile-columns: chunk 0 holds
+    # tiles [0, 1], chunk 1 holds [2, 3].  Rank 0 visits chunk 1 then chunk
+    # 0, one tile per visit; rank 1 visits chunk 0 then chunk 1.
+    G = O.Geometry(4, 4, 64, 2, 2, 2, swizzle=O.TILE_INTERLEAVED)
+    assert G.seq(0) == [2, 0, 3, 1]
+    assert G.seq(1) == [0, 2, 1, 3]
+    assert G.trace().tolist() == [2, 0, 0, 2, 3, 1, 1, 3]
+    # unequal chunks: M=6, W=2 (Mc=3), 2-row tiles: tile-rows 0 and 1 start
+    # in chunk 0, tile-row 2 in chunk 1; one tile-column.  Chunk 0 = [0, 1],
+    # chunk 1 = [2]; once chunk 1 is used up only chunk 0 is left.
+    G = O.Geometry(6, 16, 64, 2, 2, 16, swizzle=O.TILE_INTERLEAVED)
+    assert [G.chunk_tiles(d) for d in range(2)] == [[0, 1], [2]]
+    assert G.seq(0) == [2, 0, 1]
+    assert G.seq(1) == [0, 2, 1]
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_tile_interleaved_properties(g):
+    """Every rank's order is a permutation that keeps each chunk's own tile
+    order; with equal chunks the k-th tile of rank r lies in chunk
+    (r + 1 + k) mod W, so in every step the W ranks write W different
+    chunks and every chunk receives one tile per rank in every W steps."""
+    for (M, N, K, W, bm, bn) in _geom_cases() + _random_geoms():
+        G = O.Geometry(M, N, K, W, bm, bn, group_m=g, swizzle=O.TILE_INTERLEAVED)
+        tab = G.seq_table()
+        counts = [len(G.chunk_tiles(d)) for d in range(W)]
+        for r in range(W):
+            assert sorted(tab[r].tolist()) == list(range(G.T))
+            for d in range(W):
+                mine = [t for t in tab[r] if G.owner(t // G.tiles_n) == d]
+                assert mine == G.chunk_tiles(d)
+        if len(set(counts)) == 1:
+            for r in range(W):
+                for k in range(G.T):
+                    assert G.owner(tab[r, k] // G.tiles_n) == (r + 1 + k) % W
+            for k in range(G.T):
+                assert sorted(G.owner(t // G.tiles_n) for t in tab[:, k]) == list(range(W))
+
+
 def test_identity_swizzle_same_order_everywhere():
     G = O.Geometry(8 * 512, 1024, 64, 8, 256, 256, swizzle=O.IDENTITY)
     tab = G.seq_table()
@@ -392,7 +432,7 @@ TILES = [(256, 256), (64, 64)]
     (dict(order=O.TWO_LEVEL, groups=3), O.INVALID_ARG),
     (dict(order=O.TWO_LEVEL, groups=0), O.INVALID_ARG),
     (dict(order=O.TWO_LEVEL, groups=2), O.OK),
-    (dict(swizzle=3), O.INVALID_ARG),
+    (dict(swizzle=4), O.INVALID_ARG),
     (dict(has_c=1, ldc=100), O.INVALID_ARG),
     (dict(has_c=1, ldc=0), O.OK),
     (dict(has_c=1, ldc=1024), O.OK),
