@@ -70,6 +70,10 @@ extern "C" {
                                               tile goes to dest(r, k mod W)
                                               while every chunk has tiles left */
 
+/* staging element type (gemm_rs_desc_t.staging_dtype) */
+#define GEMM_RS_STAGING_F32  0
+#define GEMM_RS_STAGING_BF16 1
+
 /* ---- run flags ---------------------------------------------------------- */
 #define GEMM_RS_RUN_GEMM    1u /* GEMM + epilogue + flag publish            */
 #define GEMM_RS_RUN_REDUCE  2u /* flag-gated reduce (+ flag reset)          */
@@ -100,6 +104,13 @@ extern "C" {
  *   materialize_sub  two-level only: write each group's partial sum to a
  *                sub-group buffer with its own flags before the final sum
  *   timeout_ms   bound on every device flag wait; 0 = 1000 ms
+ *   staging_dtype  GEMM_RS_STAGING_F32 (default): partials are staged in
+ *                float32, the precision the fixed-order reduce sums in.
+ *                GEMM_RS_STAGING_BF16 (bf16 inputs only, not with
+ *                materialize_sub): each partial is rounded to bfloat16
+ *                (nearest even) when staged, halving the staging traffic
+ *                of both kernels at the cost of a second rounding per
+ *                partial; the reduce still sums in float32 in fixed order.
  */
 typedef struct gemm_rs_desc {
     int64_t M, N, K;
@@ -114,7 +125,7 @@ typedef struct gemm_rs_desc {
     int32_t materialize_sub;
     int64_t ldc;
     uint32_t timeout_ms;
-    uint32_t reserved;
+    uint32_t staging_dtype;
 } gemm_rs_desc_t;
 
 typedef struct gemm_rs_plan_s *gemm_rs_plan_t;
@@ -122,7 +133,8 @@ typedef struct gemm_rs_plan_s *gemm_rs_plan_t;
 /*
  * Introspection record (tests and benchmark).  Workspace pointers are
  * device addresses owned by the plan.
- *   staging      float32 S[d][r][Mc][N], slot (d,r) at ((d*W + r)*Mc)*N
+ *   staging      S[d][r][Mc][N] (float32, or bfloat16 bits with
+ *                GEMM_RS_STAGING_BF16), slot (d,r) at element ((d*W + r)*Mc)*N
  *   flags        uint32 flag[r][t], r < W, t < T (t = tm*tiles_n + tn)
  *   sub          float32 sub[d][g][Mc][N] (materialize_sub only, else NULL)
  *   sub_flags    uint32 subflag[g][t] (materialize_sub only, else NULL)

@@ -36,6 +36,7 @@ OK, INVALID_ARG, UNSUPPORTED, HIP_ERROR, TIMEOUT, PROTOCOL = 0, -1, -2, -3, -4, 
 BF16, F32 = 0, 1
 FLAT, TWO_LEVEL = 0, 1
 REMOTE_FIRST, SELF_FIRST, IDENTITY, TILE_INTERLEAVED = 0, 1, 2, 3
+STAGING_F32, STAGING_BF16 = 0, 1
 RUN_GEMM, RUN_REDUCE, KEEP_FLAGS, TRACE_TILES = 1, 2, 4, 8
 MAX_W = 64
 K_STEP = 64
@@ -51,7 +52,8 @@ _lib = None
 # --------------------------------------------------------------------------
 def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
              groups=1, swizzle=REMOTE_FIRST, has_c=0, ldc=0,
-             materialize_sub=0, supported_tiles: Optional[Sequence] = None):
+             materialize_sub=0, supported_tiles: Optional[Sequence] = None,
+             staging_dtype=STAGING_F32):
     """Return the status a plan must give for this descriptor.
 
     INVALID_ARG: the problem itself is ill-posed.  A reduce-scatter over W
@@ -63,11 +65,11 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     shape not in ``supported_tiles``, N not a multiple of the tile width,
     K not a multiple of the 64-deep K step, a C row pitch that is not a
     multiple of 8 elements (16-byte rows), M, N or K of 2^31 or more,
-    or a grid too large for 32-bit
-    workgroup ids.
+    a grid too large for 32-bit workgroup ids, or bfloat16 staging with
+    float32 inputs or with the materialised two-level buffers.
     """
     ints = (M, N, K, W, dtype, tile_m, tile_n, group_m, order, groups,
-            swizzle, has_c, ldc, materialize_sub)
+            swizzle, has_c, ldc, materialize_sub, staging_dtype)
     if any(not isinstance(v, (int, np.integer)) for v in ints):
         return INVALID_ARG
     if W < 1 or W > MAX_W or M < 1 or N < 1 or K < 1:
@@ -88,6 +90,8 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
         return INVALID_ARG
     if materialize_sub not in (0, 1) or (materialize_sub and order != TWO_LEVEL):
         return INVALID_ARG
+    if staging_dtype not in (STAGING_F32, STAGING_BF16):
+        return INVALID_ARG
     if supported_tiles is not None and (tile_m, tile_n) not in set(
             tuple(t) for t in supported_tiles):
         return UNSUPPORTED
@@ -96,6 +100,8 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     if N % tile_n != 0 or K % K_STEP != 0:
         return UNSUPPORTED
     if has_c and ldc % 8 != 0:
+        return UNSUPPORTED
+    if staging_dtype == STAGING_BF16 and (dtype != BF16 or materialize_sub):
         return UNSUPPORTED
     if max(M, N, K) > 2**31 - 1:
         return UNSUPPORTED
@@ -280,7 +286,7 @@ def _load():
     common = [i64, i64, i64, i32, i32, vp, vp, vp, i32, i64, dbl, dbl]
     lib.oracle_partial_rows.argtypes = common + [i32, i64, i64, vp]
     lib.oracle_reference_rows.argtypes = common + [i32, i32, i64, i64, vp]
-    lib.oracle_emulate_rows.argtypes = common + [i32, i32, i64, i64, i32, vp]
+    lib.oracle_emulate_rows.argtypes = common + [i32, i32, i64, i64, i32, i32, vp]
     lib.oracle_reference_elems.argtypes = common + [i32, i32, i64, vp, vp, vp]
     lib.oracle_reduce_emulate.argtypes = [i32, i32, i32, i64, vp, i32, vp]
     lib.oracle_bf16_rne_array.argtypes = [i64, vp, vp]
@@ -348,16 +354,19 @@ def reference_rows(A, B, C=None, *, dtype, alpha=1.0, beta=0.0, ldc=0,
 
 
 def emulate_rows(A, B, C=None, *, dtype, alpha=1.0, beta=0.0, ldc=0,
-                 order=FLAT, groups=1, row_lo=0, row_hi=None):
+                 order=FLAT, groups=1, row_lo=0, row_hi=None,
+                 staging_dtype=STAGING_F32):
     """Float-pipeline emulation of rows [row_lo, row_hi): uint16 bfloat16
-    bits for dtype BF16, float32 for F32."""
+    bits for dtype BF16, float32 for F32.  With STAGING_BF16 each rank's
+    float epilogue value is rounded to bfloat16 (nearest even) before the
+    ordered float sum, as a bfloat16 staging slot holds it."""
     keep, args, (W, M, N, K) = _common(A, B, C, dtype, alpha, beta, ldc)
     row_hi = M if row_hi is None else row_hi
     out_kind = 0 if dtype == BF16 else 1
     out = np.empty((row_hi - row_lo, N),
                    dtype=np.uint16 if out_kind == 0 else np.float32)
     rc = _load().oracle_emulate_rows(*args, order, groups, row_lo, row_hi,
-                                     out_kind, _ptr(out))
+                                     out_kind, int(staging_dtype == STAGING_BF16), _ptr(out))
     assert rc == 0, rc
     return out
 

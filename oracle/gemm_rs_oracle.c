@@ -207,16 +207,18 @@ int oracle_reference_rows(int64_t M, int64_t N, int64_t K, int32_t W,
 }
 
 /*
- * Emulate mode, rows [row_lo, row_hi): D_r rounded to float, the ordered
- * sum (same order as reference mode) in float, then bfloat16 RNE bits
- * (out_kind 0, out is uint16) or float (out_kind 1, out is float).
+ * Emulate mode, rows [row_lo, row_hi): D_r rounded to float (and, with
+ * staging_kind 1, that float rounded to bfloat16 by RNE, the value a
+ * bfloat16 staging slot holds), the ordered sum (same order as reference
+ * mode) in float, then bfloat16 RNE bits (out_kind 0, out is uint16) or
+ * float (out_kind 1, out is float).
  */
 int oracle_emulate_rows(int64_t M, int64_t N, int64_t K, int32_t W,
                         int32_t dtype, const void *A, const void *B,
                         const void *C, int32_t has_c, int64_t ldc,
                         double alpha, double beta, int32_t order,
                         int32_t groups, int64_t row_lo, int64_t row_hi,
-                        int32_t out_kind, void *out)
+                        int32_t out_kind, int32_t staging_kind, void *out)
 {
     if (check_shape(M, N, K, W, order, groups) || row_lo < 0 ||
         row_hi > M || row_lo > row_hi)
@@ -240,6 +242,8 @@ int oracle_emulate_rows(int64_t M, int64_t N, int64_t K, int32_t W,
                     int first_in_group = (r % L) == 0;
                     for (int64_t j = 0; j < N; ++j) {
                         float v = (float)d_r[j];
+                        if (staging_kind == 1)
+                            v = (float)bf16_bits_value(oracle_bf16_rne(v));
                         s_g[j] = first_in_group ? v : s_g[j] + v;
                     }
                     if ((r % L) == L - 1) {

@@ -20,7 +20,8 @@
 //   * v_mfma_f32_32x32x16_bf16, fp32 accumulators; the LDS reads of the
 //     next 16-deep slice are interleaved with the MFMAs of the current one.
 // Epilogue: alpha*acc, plus beta*C on rows whose chunk this rank owns,
-// stored as fp32 into the staging slot of each row's destination chunk
+// stored as fp32 (or, optionally, rounded to bf16) into the staging slot
+// of each row's destination chunk
 // (rows pass through LDS so that each store instruction writes whole
 // staging rows); then the tile's ready flag is published (page "flux实现：
 // sm80 gemm+rs", section "cutlass自定义epilogue–sm80": a compute node
@@ -38,6 +39,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -315,13 +317,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         x[2] = own ? y2 : x[2];
                         x[3] = own ? y3 : x[3];
                     }
-                    float *dst = a.staging +
-                                 (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
-                                 col0 + scol;
+                    const int64_t off =
+                        (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
+                        col0 + scol;
                     // whole 128-byte lines from one instruction: a streaming
-                    // store keeps the 2 GB of staging from evicting the A/B
-                    // panels other tiles are still reading
-                    __builtin_nontemporal_store(x, (f32x4_t *)dst);
+                    // store keeps the staging from evicting the A/B panels
+                    // other tiles are still reading
+                    if (a.staging_bf16) {
+                        // bfloat16 staging: each partial rounded to nearest even
+                        const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
+                        const __bf16 h2 = (__bf16)x[2], h3 = (__bf16)x[3];
+                        u32x2_t hw;
+                        hw[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        hw[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                        __builtin_nontemporal_store(hw, (u32x2_t *)((uint16_t *)a.staging + off));
+                    } else {
+                        __builtin_nontemporal_store(x, (f32x4_t *)((float *)a.staging + off));
+                    }
                 }
             }
             if (i + 1 < FM) __syncthreads();        // the stripe buffer is reused

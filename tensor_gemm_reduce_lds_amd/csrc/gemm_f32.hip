@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
         float x = a.alpha * acc[v];
         if (a.has_c && d == r) x += a.beta * Cp[row * a.ldc + col];
-        float *dst = a.staging +
+        float *dst = (float *)a.staging +
                      (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N;
         __builtin_nontemporal_store(x, dst + col);
     }

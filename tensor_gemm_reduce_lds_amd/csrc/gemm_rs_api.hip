@@ -26,7 +26,7 @@ struct gemm_rs_plan_s {
     int device;
     int32_t units_per_tile;
     uint64_t timeout_ticks;
-    float *staging;
+    void *staging;           // float or bfloat16 bits (staging_dtype)
     uint32_t *flags;         // [W][T]
     uint32_t *counters;      // [T]
     uint32_t *sub_counters;  // [G][T] (materialised two-level)
@@ -92,11 +92,16 @@ int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
     if ((d.materialize_sub != 0 && d.materialize_sub != 1) ||
         (d.materialize_sub && d.order != GEMM_RS_ORDER_TWO_LEVEL))
         return GEMM_RS_ERR_INVALID_ARG;
+    if (d.staging_dtype != GEMM_RS_STAGING_F32 && d.staging_dtype != GEMM_RS_STAGING_BF16)
+        return GEMM_RS_ERR_INVALID_ARG;
     bool tile_ok = d.dtype == GEMM_RS_BF16 ? bf16_tile_supported(bm, bn)
                                            : f32_tile_supported(bm, bn);
     if (!tile_ok) return GEMM_RS_ERR_UNSUPPORTED;
     if (d.N % bn != 0 || d.K % kKStep != 0) return GEMM_RS_ERR_UNSUPPORTED;
     if (d.has_c && d.ldc % 8 != 0) return GEMM_RS_ERR_UNSUPPORTED;
+    if (d.staging_dtype == GEMM_RS_STAGING_BF16 &&
+        (d.dtype != GEMM_RS_BF16 || d.materialize_sub))
+        return GEMM_RS_ERR_UNSUPPORTED;
     if (d.M > INT32_MAX || d.N > INT32_MAX || d.K > INT32_MAX)
         return GEMM_RS_ERR_UNSUPPORTED;
     int64_t tiles = ((d.M + bm - 1) / bm) * (d.N / bn);
@@ -199,7 +204,8 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
         rate_khz = 100000;  // the 100 MHz constant clock
     p->timeout_ticks = (uint64_t)d.timeout_ms * (uint64_t)rate_khz;
 
-    p->staging_bytes = (int64_t)d.W * d.M * d.N * 4;
+    p->staging_bytes =
+        (int64_t)d.W * d.M * d.N * (d.staging_dtype == GEMM_RS_STAGING_BF16 ? 2 : 4);
     p->flags_bytes = (int64_t)d.W * g.T * 4;
     p->counters_bytes = (int64_t)g.T * 4;
     p->trace_bytes = (int64_t)d.W * g.T * 4;
@@ -295,6 +301,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     a.has_c = p->d.has_c;
     a.alpha = alpha; a.beta = beta;
     a.staging = p->staging;
+    a.staging_bf16 = p->d.staging_dtype == GEMM_RS_STAGING_BF16;
     a.flags = p->flags;
     a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
     // every consumer runs after the producing launch completes (same stream
@@ -319,6 +326,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     r.units_per_tile = p->units_per_tile;
     r.timeout_ticks = p->timeout_ticks;
     r.staging = p->staging;
+    r.staging_bf16 = p->d.staging_dtype == GEMM_RS_STAGING_BF16;
     r.out = out;
     r.flags = p->flags;
     r.counters = p->counters;

@@ -132,7 +132,8 @@ struct GemmArgs {
     int64_t ldc;
     int32_t has_c;
     float alpha, beta;
-    float *staging;      // [W][W][Mc][N]
+    void *staging;       // [W][W][Mc][N] float, or bfloat16 bits
+    int32_t staging_bf16;   // 1: stage partials as bfloat16 (round to nearest even)
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
     int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
@@ -149,7 +150,8 @@ struct ReduceArgs {
     int32_t acquire;         // 1: producers may run concurrently
     int32_t units_per_tile;  // BM / kReduceRows
     uint64_t timeout_ticks;  // device wall-clock ticks
-    const float *staging;
+    const void *staging;     // float, or bfloat16 bits (staging_bf16)
+    int32_t staging_bf16;
     void *out;               // [M][N]
     uint32_t *flags;         // [W][T]
     uint32_t *counters;      // [T] (flat) or [G][T] (sub stage)

@@ -20,6 +20,7 @@ namespace gemm_rs {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ void record_error(int32_t *err, int code, int32_t r, int32_t t, uint32_t v) {
     if (atomicCAS(&err[0], 0, code) == 0) {
@@ -103,15 +104,33 @@ __device__ __forceinline__ void unit_rows(const TileGeom &g, int32_t tm, int32_t
     *hi = *lo + kReduceRows < tile_hi ? *lo + kReduceRows : tile_hi;
 }
 
+// Four consecutive staged elements at element index `idx`, as floats: a
+// 16-byte float load, or an 8-byte load of four bfloat16 values (exact
+// widening: a bfloat16 is the top half of a float).
+template <bool SB>
+__device__ __forceinline__ f32x4_t load_slot(const void *S, int64_t idx) {
+    if constexpr (SB) {
+        const u32x2_t h = __builtin_nontemporal_load((const u32x2_t *)((const uint16_t *)S + idx));
+        f32x4_t v;
+        v[0] = __uint_as_float(h[0] << 16);
+        v[1] = __uint_as_float(h[0] & 0xffff0000u);
+        v[2] = __uint_as_float(h[1] << 16);
+        v[3] = __uint_as_float(h[1] & 0xffff0000u);
+        return v;
+    } else {
+        return __builtin_nontemporal_load((const f32x4_t *)((const float *)S + idx));
+    }
+}
+
 // Sum of one element group (4 columns) over the W slots in the fixed order.
-// `S` points at slot (d, 0) of the element; slots are `stride` floats apart.
-template <int WT>
-__device__ __forceinline__ f32x4_t ordered_sum(const float *S, int64_t stride, int W, int L) {
+// Slot q of the element group starts at element idx + q*stride.
+template <int WT, bool SB = false>
+__device__ __forceinline__ f32x4_t ordered_sum(const void *S, int64_t idx, int64_t stride,
+                                               int W, int L) {
     if constexpr (WT > 0) {
         f32x4_t v[WT];
 #pragma unroll
-        for (int q = 0; q < WT; ++q)
-            v[q] = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
+        for (int q = 0; q < WT; ++q) v[q] = load_slot<SB>(S, idx + q * stride);
         f32x4_t y = v[0], s = v[0];
 #pragma unroll
         for (int q = 0; q < WT; ++q) {
@@ -122,7 +141,7 @@ __device__ __forceinline__ f32x4_t ordered_sum(const float *S, int64_t stride, i
     } else {
         f32x4_t y = {0, 0, 0, 0}, s = {0, 0, 0, 0};
         for (int q = 0; q < W; ++q) {
-            f32x4_t v = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
+            const f32x4_t v = load_slot<SB>(S, idx + q * stride);
             s = (q % L == 0) ? v : s + v;
             if (q % L == L - 1) y = (q / L == 0) ? s : y + s;
         }
@@ -130,16 +149,17 @@ __device__ __forceinline__ f32x4_t ordered_sum(const float *S, int64_t stride, i
     }
 }
 
-// Two elements at once (all 2*W loads issued before any add).
-template <int WT>
-__device__ __forceinline__ void ordered_sum2(const float *S, const float *S2, int64_t stride,
-                                             int W, int L, f32x4_t *y_out, f32x4_t *y2_out) {
+// Two element groups at once (all 2*W loads issued before any add).
+template <int WT, bool SB>
+__device__ __forceinline__ void ordered_sum2(const void *S, int64_t idx, int64_t idx2,
+                                             int64_t stride, int W, int L, f32x4_t *y_out,
+                                             f32x4_t *y2_out) {
     if constexpr (WT > 0) {
         f32x4_t v[WT], u[WT];
 #pragma unroll
         for (int q = 0; q < WT; ++q) {
-            v[q] = __builtin_nontemporal_load((const f32x4_t *)(S + q * stride));
-            u[q] = __builtin_nontemporal_load((const f32x4_t *)(S2 + q * stride));
+            v[q] = load_slot<SB>(S, idx + q * stride);
+            u[q] = load_slot<SB>(S, idx2 + q * stride);
         }
         f32x4_t y = v[0], s = v[0], y2 = u[0], s2 = u[0];
 #pragma unroll
@@ -154,8 +174,8 @@ __device__ __forceinline__ void ordered_sum2(const float *S, const float *S2, in
         *y_out = y;
         *y2_out = y2;
     } else {
-        *y_out = ordered_sum<0>(S, stride, W, L);
-        *y2_out = ordered_sum<0>(S2, stride, W, L);
+        *y_out = ordered_sum<0, SB>(S, idx, stride, W, L);
+        *y2_out = ordered_sum<0, SB>(S, idx2, stride, W, L);
     }
 }
 
@@ -188,7 +208,7 @@ __device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32
 }
 
 // One-stage reduce: flags -> out.
-template <int WT, bool OUT_BF16>
+template <int WT, bool OUT_BF16, bool SB>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const TileGeom &g = a.g;
     const int32_t U = a.units_per_tile;
@@ -221,16 +241,17 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     for (int64_t row = lo + threadIdx.x / C4; row < hi; row += 2 * RPP) {
         const int64_t row2 = row + RPP;
         const int64_t d = row / g.Mc;
-        const float *S = a.staging + ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
+        const int64_t idx = ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
         if (row2 < hi) {
             const int64_t d2 = row2 / g.Mc;
-            const float *S2 = a.staging + ((d2 * W) * g.Mc + (row2 - d2 * g.Mc)) * g.N + col;
+            const int64_t idx2 = ((d2 * W) * g.Mc + (row2 - d2 * g.Mc)) * g.N + col;
             f32x4_t y, y2;
-            ordered_sum2<WT>(S, S2, stride, W, L, &y, &y2);
+            ordered_sum2<WT, SB>(a.staging, idx, idx2, stride, W, L, &y, &y2);
             store_out4(a.out, row * g.N + col, y, OUT_BF16);
             store_out4(a.out, row2 * g.N + col, y2, OUT_BF16);
         } else {
-            store_out4(a.out, row * g.N + col, ordered_sum<WT>(S, stride, W, L), OUT_BF16);
+            store_out4(a.out, row * g.N + col, ordered_sum<WT, SB>(a.staging, idx, stride, W, L),
+                       OUT_BF16);
         }
     }
 }
@@ -270,8 +291,8 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
         const int64_t row = lo + e / C4;
         const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
         const int64_t d = row / g.Mc, il = row - d * g.Mc;
-        const float *S = a.staging + ((d * g.W + (int64_t)grp * L) * g.Mc + il) * g.N + col;
-        const f32x4_t s = ordered_sum<LT>(S, stride, L, L);
+        const int64_t idx = ((d * g.W + (int64_t)grp * L) * g.Mc + il) * g.N + col;
+        const f32x4_t s = ordered_sum<LT>(a.staging, idx, stride, L, L);
         float *dst = a.sub + ((d * G + grp) * g.Mc + il) * g.N + col;
         __builtin_nontemporal_store(s, (f32x4_t *)dst);
     }
@@ -309,8 +330,8 @@ __global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a
         const int64_t row = lo + e / C4;
         const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
         const int64_t d = row / g.Mc, il = row - d * g.Mc;
-        const float *S = a.sub + ((d * G) * g.Mc + il) * g.N + col;
-        const f32x4_t y = ordered_sum<0>(S, stride, G, G);
+        const int64_t idx = ((d * G) * g.Mc + il) * g.N + col;
+        const f32x4_t y = ordered_sum<0>(a.sub, idx, stride, G, G);
         store_out4(a.out, row * g.N + col, y, OUT_BF16);
     }
 }
@@ -323,7 +344,7 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     trace[b] = t;
 }
 
-template <bool BF>
+template <bool BF, bool SB>
 hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
     const int64_t units =
         a.slice_kind == kSliceLastStep ? (int64_t)(a.k_hi - a.k_lo) * a.g.W * a.units_per_tile
@@ -332,11 +353,11 @@ hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
     if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)units);
     switch (a.g.W) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((reduce_kernel<0, BF>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<0, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -344,7 +365,8 @@ hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_reduce(const ReduceArgs &a, int dtype, hipStream_t s) {
-    return dtype == GEMM_RS_BF16 ? launch_flat<true>(a, s) : launch_flat<false>(a, s);
+    if (dtype != GEMM_RS_BF16) return launch_flat<false, false>(a, s);
+    return a.staging_bf16 ? launch_flat<true, true>(a, s) : launch_flat<true, false>(a, s);
 }
 
 hipError_t launch_reduce_sub(const ReduceArgs &a, hipStream_t s) {

@@ -77,6 +77,8 @@ BAD = [
     dict(tile_m=128, tile_n=64), dict(tile_m=32, tile_n=32), dict(N=1000),
     dict(K=100), dict(has_c=1, ldc=1028), dict(dtype=1, tile_m=128, tile_n=128),
     dict(M=2**31, W=1), dict(K=2**31 + 64),
+    dict(staging_dtype=2), dict(staging_dtype=1, dtype=1, tile_m=64, tile_n=64),
+    dict(staging_dtype=1, materialize_sub=1, order=1, groups=2),
 ]
 
 

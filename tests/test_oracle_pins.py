@@ -443,9 +443,64 @@ TILES = [(256, 256), (64, 64)]
     (dict(tile_m=128, tile_n=128), O.UNSUPPORTED),
     (dict(N=1000), O.UNSUPPORTED),
     (dict(K=100), O.UNSUPPORTED),
+    (dict(swizzle=O.TILE_INTERLEAVED), O.OK),
+    (dict(staging_dtype=O.STAGING_BF16), O.OK),
+    (dict(staging_dtype=2), O.INVALID_ARG),
+    (dict(staging_dtype=O.STAGING_BF16, dtype=O.F32, tile_m=64, tile_n=64), O.UNSUPPORTED),
+    (dict(staging_dtype=O.STAGING_BF16, materialize_sub=1, order=O.TWO_LEVEL,
+          groups=2), O.UNSUPPORTED),
 ])
 def test_validate_table(kw, code):
     base = dict(M=2048, N=1024, K=512, W=8, dtype=O.BF16, tile_m=256,
                 tile_n=256)
     base.update(kw)
     assert O.validate(**base, supported_tiles=TILES) == code
+
+
+# ------------------------------------------------------ bfloat16 staging mode
+def test_bf16_staging_hand_example():
+    """W=2, K=2, one row per chunk.  Row 0's partials are 256+1 = 257 (rank 0)
+    and 256+5 = 261 (rank 1).  Staged in bfloat16 they become 256 and 260
+    (both ties, rounded to even), summing to 516 = 0x4401; staged in float
+    the sum 518 rounds (tie, to even) to 520 = 0x4402 on output."""
+    bf = lambda v: O.bf16_rne(np.array(v, np.float32)).reshape(np.shape(v))
+    A = np.stack([bf([[256, 1], [1, 0]]), bf([[256, 5], [2, 0]])])   # [W][M][K]
+    B = np.stack([bf([[1], [1]]), bf([[1], [1]])])                  # [W][K][N]
+    f32 = O.emulate_rows(A, B, dtype=O.BF16)
+    b16 = O.emulate_rows(A, B, dtype=O.BF16, staging_dtype=O.STAGING_BF16)
+    assert f32[:, 0].tolist() == [0x4402, int(bf([3.0])[0])]
+    assert b16[:, 0].tolist() == [0x4401, int(bf([3.0])[0])]
+
+
+def test_bf16_staging_equals_f32_staging_when_partials_are_exact():
+    """Integer inputs whose every partial lies in [-256, 256] are exact in
+    bfloat16, so rounding them on staging changes nothing."""
+    rng = np.random.default_rng(7)
+    W, M, N, K = 4, 8, 16, 64
+    vals = rng.integers(-1, 2, size=(W, M, K)).astype(np.float32)
+    wts = rng.integers(-1, 2, size=(W, K, N)).astype(np.float32)
+    A, B = O.bf16_rne(vals).reshape(vals.shape), O.bf16_rne(wts).reshape(wts.shape)
+    for r in range(W):
+        assert np.abs(O.partial_rows(A, B, dtype=O.BF16, r=r)).max() <= 256
+    a = O.emulate_rows(A, B, dtype=O.BF16)
+    b = O.emulate_rows(A, B, dtype=O.BF16, staging_dtype=O.STAGING_BF16)
+    assert np.array_equal(a, b)
+
+
+def test_bf16_staging_within_rounding_bound():
+    """|out - ref| <= 2^-8 |ref| + 2^-8 (1 + 2^-8) sum_r |D_r| (+ float sums):
+    each staged partial and the output are rounded to 8 significant bits
+    by round-to-nearest-even."""
+    x = I.make_inputs(I.with_shape(I.WORKLOADS["llama8b"], M=64, N=128, K=256))
+    A, B = x["A"], x["B"]
+    W = A.shape[0]
+    out = O.bf16_bits_to_f64(O.emulate_rows(A, B, dtype=O.BF16,
+                                            staging_dtype=O.STAGING_BF16))
+    ref = O.reference_rows(A, B, dtype=O.BF16)
+    mag = sum(np.abs(O.partial_rows(A, B, dtype=O.BF16, r=r)) for r in range(W))
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -8 * (1 + 2.0 ** -8) * mag + 1e-6 * mag
+    assert np.all(np.abs(out - ref) <= bound)
+    # and the second rounding is visible: not every output equals the
+    # float-staged one
+    f32 = O.bf16_bits_to_f64(O.emulate_rows(A, B, dtype=O.BF16))
+    assert np.any(out != f32)
