@@ -425,3 +425,77 @@ def max_norm_err(got, ref) -> float:
     if got.size == 0:
         return 0.0
     return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
+
+
+# --------------------------------------------------------------------------
+# all-gather + GEMM (include/gemm_ag.h)
+# --------------------------------------------------------------------------
+# pieces each tile-row of X is copied in (an implementation limit of the
+# library's copy kernel, mirrored here only for the descriptor rules)
+AG_COPY_PIECES = 16
+
+
+def validate_ag(M, N, K, W, tile_m, tile_n, group_m=0, pad=0,
+                supported_tiles: Optional[Sequence] = None):
+    """Status a plan of the all-gather + GEMM must give.  INVALID_ARG: the
+    gather hands every rank an equal row shard, so M % W != 0 is invalid
+    (page "flux精读", section 3 Design: the input is all-gathered across
+    the TP group); negative sizes or a non-zero pad.  UNSUPPORTED: the tile
+    and K-step limits of the GEMM kernel, as in ``validate``."""
+    ints = (M, N, K, W, tile_m, tile_n, group_m, pad)
+    if any(not isinstance(v, (int, np.integer)) for v in ints):
+        return INVALID_ARG
+    if W < 1 or W > MAX_W or M < 1 or N < 1 or K < 1:
+        return INVALID_ARG
+    if M % W != 0:
+        return INVALID_ARG
+    if group_m < 0 or tile_m < 0 or tile_n < 0 or pad != 0:
+        return INVALID_ARG
+    if supported_tiles is not None and (tile_m, tile_n) not in set(
+            tuple(t) for t in supported_tiles):
+        return UNSUPPORTED
+    if tile_m == 0 or tile_n == 0 or N % tile_n != 0 or K % K_STEP != 0:
+        return UNSUPPORTED
+    if max(M, N, K) > 2**31 - 1:
+        return UNSUPPORTED
+    if -(-M // tile_m) * (N // tile_n) * W > 2**31 - 1:
+        return UNSUPPORTED
+    # the gather is issued as AG_COPY_PIECES pieces per tile-row and rank,
+    # counted in 32 bits
+    if -(-M // tile_m) * W * AG_COPY_PIECES > 2**32 - 1:
+        return UNSUPPORTED
+    return OK
+
+
+def ag_gather(X_shards: np.ndarray) -> np.ndarray:
+    """The all-gathered input: shard d (rank d's M/W rows) becomes rows
+    [d*M/W, (d+1)*M/W) of X (page "flux精读", section 3 Design)."""
+    W, Mc, K = X_shards.shape
+    return np.concatenate([X_shards[d] for d in range(W)], axis=0)
+
+
+def ag_send_order(M, W, tile_m, r) -> List[int]:
+    """Tile-rows of X in the order they are sent to rank r: its own chunk
+    first, then chunks r+1, r+2, ... (mod W), each chunk's tile-rows in
+    ascending order; a tile-row belongs to the chunk of its first row.  The
+    GEMM's tiles wait in the same order (page "flux精读", section 3 Design:
+    the wait order follows the send order)."""
+    G = Geometry(M, tile_m, K_STEP, W, tile_m, tile_m, swizzle=SELF_FIRST)
+    out = []
+    for s in range(W):
+        out.extend(G.chunk_tile_rows(G.dest(r, s)))
+    return out
+
+
+def ag_gemm_rows(X_shards, B, *, r, row_lo=0, row_hi=None) -> np.ndarray:
+    """Rank r's output rows [row_lo, row_hi) of Y_r = X . B_r, fp64, where X
+    is the gathered input (bfloat16 bit patterns in, as everywhere)."""
+    X_shards = np.ascontiguousarray(X_shards)
+    W, Mc, K = X_shards.shape
+    # stacked row shards already are the gathered matrix, row for row (the
+    # same rows as ag_gather, without a copy)
+    X = X_shards.reshape(W * Mc, K)
+    M = X.shape[0]
+    row_hi = M if row_hi is None else row_hi
+    return partial_rows(X[None], np.asarray(B)[r][None], dtype=BF16, r=0,
+                        row_lo=row_lo, row_hi=row_hi)

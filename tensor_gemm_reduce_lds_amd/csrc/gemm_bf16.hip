@@ -107,6 +107,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
+    if (a.signals) {
+        // all-gather mode: wait until this tile-row of A has been copied in
+        // (agent-scope acquire, bounded); the loads below then see it
+        int failed = 0;
+        if (tid == 0) {
+            const uint32_t *sig = a.signals + (int64_t)r * g.tiles_m + tm;
+            const uint64_t t0 = wall_clock64();
+            while (__hip_atomic_load(sig, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
+                   a.epoch) {
+                if (wall_clock64() - t0 > a.timeout_ticks) {
+                    failed = 1;
+                    if (atomicCAS(&a.err[0], 0, GEMM_RS_ERR_TIMEOUT) == 0) {
+                        __hip_atomic_store(&a.err[1], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&a.err[2], tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&a.err[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+        }
+        if (__syncthreads_or(failed)) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+
     const uint16_t *A = (const uint16_t *)a.A + (int64_t)r * g.M * g.K;
     const uint16_t *B = (const uint16_t *)a.B + (int64_t)r * g.K * g.N;
     const int64_t row0 = (int64_t)tm * BM, col0 = (int64_t)tn * BN;
@@ -318,8 +343,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         x[3] = own ? y3 : x[3];
                     }
                     const int64_t off =
-                        (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
-                        col0 + scol;
+                        a.plain_out
+                            ? ((int64_t)r * g.M + row) * g.N + col0 + scol
+                            : (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
+                                  col0 + scol;
                     // whole 128-byte lines from one instruction: a streaming
                     // store keeps the staging from evicting the A/B panels
                     // other tiles are still reading
@@ -350,7 +377,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // tile's stores are written back past this XCD's L2 first).  When the
     // consumer is stream-ordered after this kernel, the kernel boundary
     // already makes the stores visible and the flag is a plain store.
-    if (a.release_flags) {
+    if (!a.flags) {
+        // all-gather mode: an ordinary output tile, no flag
+    } else if (a.release_flags) {
         __threadfence();
         __syncthreads();
         if (tid == 0)

@@ -294,7 +294,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     if (do_reduce && (!out || !aligned16(out))) return GEMM_RS_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
 
-    GemmArgs a;
+    GemmArgs a = {};   // fields this path does not use stay zero (no gate, no plain output)
     a.g = p->g;
     a.A = A; a.B = B; a.C = C;
     a.ldc = p->d.ldc;
@@ -317,7 +317,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         return p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(x, st) : launch_gemm_f32(x, st);
     };
 
-    ReduceArgs r;
+    ReduceArgs r = {};
     r.g = p->g;
     r.order = p->d.order;
     r.groups = p->d.groups;

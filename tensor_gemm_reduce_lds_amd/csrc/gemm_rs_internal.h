@@ -139,6 +139,15 @@ struct GemmArgs {
     int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
     uint32_t b_offset;      // workgroup b = b_offset + blockIdx.x (launch slices)
     uint32_t n_blocks;      // workgroups in this launch
+    // all-gather mode (gemm_ag_*): tiles are stored as bfloat16 to
+    // staging[r][row][col] (no chunk routing, flags == null), and a tile
+    // first waits until signals[r*tiles_m + tm] == epoch, i.e. its rows of
+    // A have arrived (bounded by timeout_ticks; a timeout is recorded in err)
+    int32_t plain_out;
+    const uint32_t *signals;
+    uint32_t epoch;
+    uint64_t timeout_ticks;
+    int32_t *err;
 };
 
 enum { kSliceAll = 0, kSliceLastStep = 1, kSliceSteps = 2 };

@@ -16,6 +16,7 @@ from typing import Optional
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libgemm_rs.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "gemm_rs.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(_PKG), "include", "gemm_ag.h")]
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -30,6 +31,8 @@ SWIZZLE_REMOTE_FIRST, SWIZZLE_SELF_FIRST, SWIZZLE_IDENTITY, SWIZZLE_TILE_INTERLE
 STAGING_F32, STAGING_BF16 = 0, 1
 RUN_GEMM, RUN_REDUCE, KEEP_FLAGS, TRACE_TILES, OVERLAP_REDUCE = 1, 2, 4, 8, 16
 RUN_ALL = RUN_GEMM | RUN_REDUCE
+AG_RUN_COPY, AG_RUN_GEMM, AG_FUSED, AG_EXPECT_NEXT = 1, 2, 4, 8
+AG_RUN_ALL = AG_RUN_COPY | AG_RUN_GEMM
 
 
 class gemm_rs_desc_t(ctypes.Structure):
@@ -57,6 +60,24 @@ class gemm_rs_info_t(ctypes.Structure):
         ("trace", ctypes.c_void_p),
         ("staging_bytes", ctypes.c_int64), ("flags_bytes", ctypes.c_int64),
         ("sub_bytes", ctypes.c_int64), ("sub_flags_bytes", ctypes.c_int64),
+    ]
+
+
+class gemm_ag_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("W", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("group_m", ctypes.c_int32), ("timeout_ms", ctypes.c_uint32), ("pad", ctypes.c_uint32),
+    ]
+
+
+class gemm_ag_info_t(ctypes.Structure):
+    _fields_ = [
+        ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
+        ("group_m", ctypes.c_int32), ("epoch", ctypes.c_uint32),
+        ("gathered", ctypes.c_void_p), ("signals", ctypes.c_void_p),
+        ("gathered_bytes", ctypes.c_int64),
     ]
 
 
@@ -91,17 +112,26 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gemm_rs_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gemm_rs_strerror.argtypes = [ctypes.c_int]
     lib.gemm_rs_strerror.restype = ctypes.c_char_p
+    lib.gemm_ag_plan.argtypes = [ctypes.POINTER(gemm_ag_desc_t), ctypes.POINTER(vp)]
+    lib.gemm_ag_run.argtypes = [vp, vp, vp, vp, vp, u32]
+    lib.gemm_ag_query.argtypes = [vp, ctypes.POINTER(gemm_ag_info_t)]
+    lib.gemm_ag_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.gemm_ag_destroy.argtypes = [vp]
     for f in ("gemm_rs_plan", "gemm_rs_run", "gemm_rs_destroy", "gemm_rs_query",
-              "gemm_rs_tile_order", "gemm_rs_status"):
+              "gemm_rs_tile_order", "gemm_rs_status", "gemm_ag_plan", "gemm_ag_run",
+              "gemm_ag_query", "gemm_ag_status", "gemm_ag_destroy"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
 
 
-def header_functions(path: str = HEADER):
-    """Names of the functions the public header declares."""
-    text = open(path).read()
-    return sorted(set(re.findall(r"GEMM_RS_API\s+[\w\s\*]+?\b(gemm_rs_\w+)\s*\(", text)))
+def header_functions(paths=None):
+    """Names of the functions the public headers declare."""
+    names = set()
+    for path in paths or HEADERS:
+        text = open(path).read()
+        names.update(re.findall(r"GEMM_RS_API\s+[\w\s\*]+?\b(gemm_(?:rs|ag)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 class GemmRsError(RuntimeError):
@@ -212,6 +242,87 @@ class Plan:
     def close(self):
         if self.handle is not None:
             gemm_rs_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- all-gather + GEMM (include/gemm_ag.h), same names ------------------------
+def make_ag_desc(M, N, K, W, tile_m=0, tile_n=0, group_m=0, timeout_ms=0,
+                 pad=0) -> gemm_ag_desc_t:
+    return gemm_ag_desc_t(M=M, N=N, K=K, W=W, tile_m=tile_m, tile_n=tile_n,
+                          group_m=group_m, timeout_ms=timeout_ms, pad=pad)
+
+
+def gemm_ag_plan(desc: Optional[gemm_ag_desc_t]):
+    """Returns (status, plan handle or None)."""
+    h = ctypes.c_void_p()
+    rc = load_library().gemm_ag_plan(None if desc is None else ctypes.byref(desc),
+                                     ctypes.byref(h))
+    return rc, h.value
+
+
+def gemm_ag_run(plan, X, B, out, stream=None, run_flags=AG_RUN_ALL | AG_FUSED) -> int:
+    return load_library().gemm_ag_run(plan, _ptr(X), _ptr(B), _ptr(out),
+                                      _stream_handle(stream), run_flags)
+
+
+def gemm_ag_query(plan):
+    """Returns (status, gemm_ag_info_t)."""
+    info = gemm_ag_info_t()
+    rc = load_library().gemm_ag_query(plan, ctypes.byref(info))
+    return rc, info
+
+
+def gemm_ag_status(plan, stream=None):
+    """Returns (status, [code, rank, tile-row, 0])."""
+    detail = (ctypes.c_int32 * 4)()
+    rc = load_library().gemm_ag_status(plan, _stream_handle(stream), detail)
+    return rc, list(detail)
+
+
+def gemm_ag_destroy(plan) -> int:
+    return load_library().gemm_ag_destroy(plan)
+
+
+class AgPlan:
+    """Owns one all-gather + GEMM plan; raises GemmRsError on a non-OK status."""
+
+    def __init__(self, **desc_fields):
+        self.desc = make_ag_desc(**desc_fields)
+        rc, h = gemm_ag_plan(self.desc)
+        if rc != OK:
+            raise GemmRsError(rc, "gemm_ag_plan")
+        self.handle = h
+
+    @property
+    def info(self) -> gemm_ag_info_t:
+        rc, info = gemm_ag_query(self.handle)
+        if rc != OK:
+            raise GemmRsError(rc, "gemm_ag_query")
+        return info
+
+    def run(self, X, B, out, stream=None, run_flags=AG_RUN_ALL | AG_FUSED):
+        rc = gemm_ag_run(self.handle, X, B, out, stream, run_flags)
+        if rc != OK:
+            raise GemmRsError(rc, "gemm_ag_run")
+
+    def status(self, stream=None):
+        return gemm_ag_status(self.handle, stream)
+
+    def close(self):
+        if self.handle is not None:
+            gemm_ag_destroy(self.handle)
             self.handle = None
 
     def __enter__(self):

@@ -154,3 +154,30 @@ def make_inputs(w: Workload, seed: int = 0, dist: Optional[str] = None,
 def with_shape(w: Workload, **kw) -> Workload:
     """A copy of a workload with some fields replaced (for smaller cases)."""
     return dataclasses.replace(w, **kw)
+
+
+# ---- all-gather + GEMM inputs -------------------------------------------------
+# FFN up-projection shard of a Llama-3-70B-like layer (hidden 8192, intermediate
+# 28672 split over W=8 ranks): X is sequence-sharded by rows across the ranks,
+# each rank's weight shard B_r is [K, N] with N = 28672 / 8.
+AG_WORKLOADS = {
+    "llama70b_up": dict(index=5, W=8, M=8192, N=3584, K=8192),
+}
+
+
+def make_ag_inputs(M: int, N: int, K: int, W: int, index: int = 5, seed: int = 0,
+                   dist: str = "normal"):
+    """Return dict(X=[W, M/W, K], B=[W, K, N]) as bfloat16 bits.
+
+    Rank d's row shard X[d] is rows [d*M/W, (d+1)*M/W) of the full input.
+    X ~ N(0,1), B ~ N(0, (1/sqrt(K))^2) with "normal"; "ternary" draws both
+    from {-1, 0, 1}.  Streams as in ``make_inputs`` (kind A for X, B for B).
+    """
+    Mc = M // W
+    X = np.empty((W, Mc, K), dtype=np.float32)
+    B = np.empty((W, K, N), dtype=np.float32)
+    b_scale = 1.0 / np.sqrt(K) if dist == "normal" else 1.0
+    for r in range(W):
+        X[r] = _draw(_rng(seed, index, KIND_A, r), (Mc, K), dist, 1.0)
+        B[r] = _draw(_rng(seed, index, KIND_B, r), (K, N), dist, b_scale)
+    return dict(X=to_bf16_bits(X).reshape(X.shape), B=to_bf16_bits(B).reshape(B.shape))

@@ -18,24 +18,26 @@ def test_library_exports_every_header_function():
     names = G.header_functions()
     assert names == sorted(["gemm_rs_plan", "gemm_rs_run", "gemm_rs_destroy",
                             "gemm_rs_query", "gemm_rs_tile_order",
-                            "gemm_rs_status", "gemm_rs_strerror"])
+                            "gemm_rs_status", "gemm_rs_strerror",
+                            "gemm_ag_plan", "gemm_ag_run", "gemm_ag_query",
+                            "gemm_ag_status", "gemm_ag_destroy"])
     lib = G.load_library()
     for n in names:
         assert hasattr(lib, n), n
 
 
+STRUCTS = [("d", "gemm_rs_desc_t", G.gemm_rs_desc_t), ("i", "gemm_rs_info_t", G.gemm_rs_info_t),
+           ("ad", "gemm_ag_desc_t", G.gemm_ag_desc_t), ("ai", "gemm_ag_info_t", G.gemm_ag_info_t)]
+
+
 def _c_layout(tmp_path):
     """sizeof/offsetof of the public structs as gcc lays them out."""
-    fields_d = [f[0] for f in G.gemm_rs_desc_t._fields_]
-    fields_i = [f[0] for f in G.gemm_rs_info_t._fields_]
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "gemm_rs.h"',
-           "int main(void) {",
-           '  printf("desc %zu\\n", sizeof(gemm_rs_desc_t));',
-           '  printf("info %zu\\n", sizeof(gemm_rs_info_t));']
-    for f in fields_d:
-        src.append('  printf("d.%s %%zu\\n", offsetof(gemm_rs_desc_t, %s));' % (f, f))
-    for f in fields_i:
-        src.append('  printf("i.%s %%zu\\n", offsetof(gemm_rs_info_t, %s));' % (f, f))
+           '#include "gemm_ag.h"', "int main(void) {"]
+    for key, cname, cls in STRUCTS:
+        src.append('  printf("%s %%zu\\n", sizeof(%s));' % (key, cname))
+        for f, _ in cls._fields_:
+            src.append('  printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (key, f, cname, f))
     src.append("  return 0; }")
     c = tmp_path / "layout.c"
     c.write_text("\n".join(src))
@@ -48,12 +50,10 @@ def _c_layout(tmp_path):
 
 def test_struct_layout_matches_c_compiler(tmp_path):
     lay = _c_layout(tmp_path)
-    assert int(lay["desc"]) == ctypes.sizeof(G.gemm_rs_desc_t)
-    assert int(lay["info"]) == ctypes.sizeof(G.gemm_rs_info_t)
-    for f, _ in G.gemm_rs_desc_t._fields_:
-        assert int(lay["d." + f]) == getattr(G.gemm_rs_desc_t, f).offset, f
-    for f, _ in G.gemm_rs_info_t._fields_:
-        assert int(lay["i." + f]) == getattr(G.gemm_rs_info_t, f).offset, f
+    for key, cname, cls in STRUCTS:
+        assert int(lay[key]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(lay[key + "." + f]) == getattr(cls, f).offset, (cname, f)
 
 
 def test_strerror_and_null_handles():
@@ -90,4 +90,30 @@ def test_bad_descriptors_rejected_like_oracle(kw):
     want = O.validate(**base, supported_tiles=tiles)
     assert want != O.OK
     rc, h = G.gemm_rs_plan(G.make_desc(**base))
+    assert rc == want and h is None
+
+
+def test_ag_null_handles_and_flags():
+    rc, h = G.gemm_ag_plan(None)
+    assert rc == G.ERR_INVALID_ARG and h is None
+    assert G.gemm_ag_run(None, None, None, None) == G.ERR_INVALID_ARG
+    assert G.gemm_ag_query(None)[0] == G.ERR_INVALID_ARG
+    assert G.gemm_ag_status(None)[0] == G.ERR_INVALID_ARG
+    assert G.gemm_ag_destroy(None) == G.OK
+
+
+AG_BAD = [dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=0), dict(pad=1),
+          dict(group_m=-1), dict(tile_m=-64), dict(tile_m=128, tile_n=64), dict(N=1000),
+          dict(K=100), dict(M=2**31, W=1),
+          # 2^23 tile-rows x 64 ranks x 16 copy pieces overflows 32 bits
+          dict(M=2**29, N=128, K=64, W=64, tile_m=64, tile_n=128)]
+
+
+@pytest.mark.parametrize("kw", AG_BAD)
+def test_bad_ag_descriptors_rejected_like_oracle(kw):
+    base = dict(M=2048, N=1024, K=512, W=8, tile_m=256, tile_n=256)
+    base.update(kw)
+    want = O.validate_ag(**base, supported_tiles=BF16_TILES)
+    assert want != O.OK
+    rc, h = G.gemm_ag_plan(G.make_ag_desc(**base))
     assert rc == want and h is None

@@ -504,3 +504,60 @@ def test_bf16_staging_within_rounding_bound():
     # float-staged one
     f32 = O.bf16_bits_to_f64(O.emulate_rows(A, B, dtype=O.BF16))
     assert np.any(out != f32)
+
+
+# ------------------------------------------------------ all-gather + GEMM
+def test_ag_gather_and_send_order_hand_examples():
+    shards = np.arange(2 * 3 * 2).reshape(2, 3, 2)
+    assert O.ag_gather(shards).tolist() == [[0, 1], [2, 3], [4, 5], [6, 7], [8, 9], [10, 11]]
+    # M=8, W=2, 2-row tiles: chunk 0 = tile-rows {0,1}, chunk 1 = {2,3}
+    assert O.ag_send_order(8, 2, 2, 0) == [0, 1, 2, 3]
+    assert O.ag_send_order(8, 2, 2, 1) == [2, 3, 0, 1]
+    # M=6 (Mc=3): tile-row 1 (rows 2-3) starts in chunk 0, so chunk 0 sends
+    # tile-rows {0,1} and chunk 1 only {2}
+    assert O.ag_send_order(6, 2, 2, 0) == [0, 1, 2]
+    assert O.ag_send_order(6, 2, 2, 1) == [2, 0, 1]
+
+
+def test_ag_send_order_is_a_permutation_own_chunk_first():
+    for (M, N, K, W, bm, bn) in _random_geoms(20):
+        G = O.Geometry(M, N, K, W, bm, bn)
+        for r in range(W):
+            order = O.ag_send_order(M, W, bm, r)
+            assert sorted(order) == list(range(G.tiles_m))
+            own = G.chunk_tile_rows(r)
+            assert order[:len(own)] == own
+
+
+def test_ag_gemm_rows_exact_integers():
+    """Y_r = gather(X) . B_r against an integer matmul done here in int64
+    (entries in {-1,0,1} and small integers: exact in bfloat16 and fp64)."""
+    rng = np.random.default_rng(3)
+    W, Mc, K, N = 4, 5, 64, 24
+    Xi = rng.integers(-1, 2, size=(W, Mc, K))
+    Bi = rng.integers(-3, 4, size=(W, K, N))
+    to_bits = lambda a: O.bf16_rne(a.astype(np.float32)).reshape(a.shape)
+    Xfull = np.concatenate(list(Xi), axis=0).astype(np.int64)
+    for r in range(W):
+        got = O.ag_gemm_rows(to_bits(Xi), to_bits(Bi), r=r)
+        want = Xfull @ Bi[r].astype(np.int64)
+        assert np.array_equal(got, want.astype(np.float64)), r
+    # a row range
+    got = O.ag_gemm_rows(to_bits(Xi), to_bits(Bi), r=2, row_lo=7, row_hi=12)
+    assert np.array_equal(got, (Xfull @ Bi[2].astype(np.int64))[7:12].astype(np.float64))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), O.OK),
+    (dict(W=0), O.INVALID_ARG),
+    (dict(M=1000, W=3), O.INVALID_ARG),
+    (dict(pad=1), O.INVALID_ARG),
+    (dict(group_m=-1), O.INVALID_ARG),
+    (dict(N=1000), O.UNSUPPORTED),
+    (dict(K=100), O.UNSUPPORTED),
+    (dict(tile_m=128, tile_n=64), O.UNSUPPORTED),
+])
+def test_validate_ag_table(kw, code):
+    base = dict(M=2048, N=1024, K=512, W=8, tile_m=256, tile_n=256)
+    base.update(kw)
+    assert O.validate_ag(**base, supported_tiles=[(256, 256), (256, 128)]) == code
