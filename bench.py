@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the overlapped-reduce timing (profiling runs: every "
                          "GEMM and reduce launch is then a full launch)")
+    ap.add_argument("--ag-only", action="store_true",
+                    help="time only the all-gather + GEMM half and print its object "
+                         "(profiling runs of that path)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="MiB: run one plain device copy of this size first "
                          "(reference point for HBM byte counters)")
@@ -184,6 +187,11 @@ def main():
 
     from tensor_gemm_reduce_lds_amd import gemm_rs as G
     from tensor_gemm_reduce_lds_amd import inputs as I
+
+    if args.ag_only:
+        print(json.dumps({"ag_gemm": ag_measure(args.steps, torch.cuda.current_stream())}),
+              flush=True)
+        return
 
     w = I.WORKLOADS[args.workload]
     log("bench: workload", w)
