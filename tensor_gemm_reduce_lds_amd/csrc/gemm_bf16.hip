@@ -100,7 +100,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 
     const TileGeom &g = a.g;
     int32_t r, t;
-    const uint32_t b = a.b_offset + blockIdx.x;
+    const uint32_t b = a.xcd_rank_major ? logical_block(g, a.b_offset, a.n_blocks, blockIdx.x)
+                                        : a.b_offset + blockIdx.x;
     tile_of_block(g, b, &r, &t);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
     const int tid = threadIdx.x, lane = tid & 63;

@@ -309,6 +309,9 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     a.release_flags = 0;
     a.b_offset = 0;
     a.n_blocks = (uint32_t)((int64_t)p->g.W * p->g.T);
+    // the W virtual ranks share one GPU: run them rank after rank across
+    // the XCDs (each rank's own tile order is unchanged)
+    a.xcd_rank_major = 1;
     auto gemm = [&](uint32_t b_lo, uint32_t b_hi, hipStream_t st) {
         GemmArgs x = a;
         x.b_offset = b_lo;

@@ -124,6 +124,26 @@ __host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
     *tile = 0;   // unreachable for b < W*T
 }
 
+// Logical block of the h-th workgroup of a launch that covers logical
+// blocks [b_offset, b_offset + n) (logical block k*W + r is rank r's k-th
+// tile).  The hardware hands a launch's workgroups to the 8 XCDs round
+// robin (h % 8).  When each rank's share of the launch, n/W tiles, splits
+// evenly over the XCDs, XCD x takes the x-th eighth of every rank's part of
+// the order, rank after rank: all XCDs then work on one rank's operands at a
+// time, so the memory-side cache can serve that rank's B to every XCD after
+// one read from HBM, while each XCD's L2 keeps its own tile-rows of A.  Every rank's tile order is unchanged.  Otherwise the
+// identity.  A bijection of [0, n) in both cases.
+__host__ __device__ inline uint32_t logical_block(const TileGeom &g, uint32_t b_offset,
+                                                  uint32_t n, uint32_t h) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t W = (uint32_t)g.W;
+    if (b_offset % W != 0 || n % (kXcds * W) != 0) return b_offset + h;
+    const uint32_t per = n / (kXcds * W);   // tiles of one rank per XCD
+    const uint32_t x = h % kXcds, j = h / kXcds;
+    const uint32_t r = j / per, k = x * per + j % per;
+    return b_offset + k * W + r;
+}
+
 struct GemmArgs {
     TileGeom g;
     const void *A;       // [W][M][K]
@@ -137,8 +157,9 @@ struct GemmArgs {
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
     int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
-    uint32_t b_offset;      // workgroup b = b_offset + blockIdx.x (launch slices)
+    uint32_t b_offset;      // first logical block of this launch (launch slices)
     uint32_t n_blocks;      // workgroups in this launch
+    int32_t xcd_rank_major; // 1: logical_block's XCD map, 0: block = b_offset + blockIdx.x
     // all-gather mode (gemm_ag_*): tiles are stored as bfloat16 to
     // staging[r][row][col] (no chunk routing, flags == null), and a tile
     // first waits until signals[r*tiles_m + tm] == epoch, i.e. its rows of

@@ -108,8 +108,13 @@ def test_tile_order_matches_oracle_bit_exact(name, over):
 
 
 @pytest.mark.parametrize("swizzle", [G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_TILE_INTERLEAVED])
-def test_gemm_trace_matches_oracle(swizzle):
-    w = dict(SMALL)["bf16_256x256_ragged"]
+@pytest.mark.parametrize("case", ["bf16_256x256_ragged", "llama8b"])
+def test_gemm_trace_matches_oracle(case, swizzle):
+    """Every logical block (rank r's k-th tile) is run exactly once and takes
+    the oracle's tile.  The launch hands each XCD one eighth of every rank's
+    order, rank after rank (one tile per rank and XCD in the small case, 32
+    in the 8B-like shard); the trace is indexed by logical block."""
+    w = dict(SMALL)[case] if case in dict(SMALL) else W70[case]
     x = I.make_inputs(w)
     dev = to_device(x, w)
     say("gemm trace", w.name, "swizzle", swizzle)
