@@ -219,30 +219,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // Operand fragments are double-buffered in registers: the LDS reads of
     // the next 16-deep slice are interleaved one by one with the MFMAs of
     // the current slice, so their latency hides behind the matrix pipe.
-    auto compute = [&](int buf) {
-        lds_char *S = smem + buf * STAGE;
-        bf16x8_t af[2][FM], bfr[2][FN];
-        load_frags(S, 0, af[0], bfr[0]);
+    // Each step's last slice is issued after the next step's barrier: its
+    // fragments are already in registers, and its MFMAs cover the latency
+    // of the next step's first reads, so the matrix pipes do not drain at
+    // every barrier.
+    constexpr int KS = BK / 16;
+    static_assert(KS % 2 == 0, "the last slice uses fragment buffer 1");
+    bf16x8_t af[2][FM], bfr[2][FN];
+    auto mfmas = [&](int fb) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            if (ks + 1 < BK / 16) load_frags(S, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j)
+                // operands swapped: the block comes out transposed, so a
+                // lane holds one output row and runs of 4 columns
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
+    };
+    auto interleave = [&] {
+        // schedule: one LDS read (mask 0x100), one MFMA (0x008), ...
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    // operands swapped: the block comes out transposed, so a
-                    // lane holds one output row and runs of 4 columns
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        bfr[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
-            if (ks + 1 < BK / 16) {
-                // schedule: one LDS read (mask 0x100), one MFMA (0x008), ...
-#pragma unroll
-                for (int k = 0; k < FM + 2 * FN; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < FM + 2 * FN; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     };
 
@@ -257,9 +256,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         const int ahead = KT - 1 - kt;
         wait_groups<PER, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
         __syncthreads();
+        lds_char *S = smem + (kt % STAGES) * STAGE;
+        load_frags(S, 0, af[0], bfr[0]);
+        if (kt > 0) mfmas(1);   // the previous step's last slice
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-        compute(kt % STAGES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            load_frags(S, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+            mfmas(ks & 1);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    if (KT > 0) mfmas(1);   // the last step's last slice
 
     // ---- epilogue: D = alpha*acc (+ beta*C on owned rows), scatter ----
     // The accumulators go out through LDS one 32-row stripe at a time so

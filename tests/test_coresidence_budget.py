@@ -1,0 +1,68 @@
+"""The all-gather's fused mode needs the copy kernel to run beside gated
+GEMM workgroups that occupy every CU while they wait for its signals.  A
+copy wave therefore has to fit in the registers each GEMM tile
+configuration leaves free on a SIMD at that configuration's maximum
+occupancy.  This reads the compiler's resource report for both device
+sources (built with the library's flags) and checks the budget for every
+GEMM instantiation (CPU only: hipcc cross-compiles for gfx950)."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from tensor_gemm_reduce_lds_amd import build as B
+
+VGPRS_PER_SIMD_LANE = 512      # unified VGPR + AGPR file per SIMD lane (gfx950)
+LDS_PER_CU = 160 * 1024
+SIMDS_PER_CU = 4
+GRANULE = 8
+
+
+def _report(src):
+    cmd = [B.HIPCC] + B.CFLAGS + ["--cuda-device-only", "-c", "-o", os.devnull,
+                                  "-Rpass-analysis=kernel-resource-usage", src]
+    p = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert p.returncode == 0, p.stderr[-2000:]
+    kernels, cur = {}, None
+    for line in p.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]): (\d+)",
+                      line)
+        if m and cur is not None:
+            cur[m.group(1).split(" ")[0]] = int(m.group(2))
+    return kernels
+
+
+def _alloc(vgprs, agprs):
+    # AGPRs start at the next multiple of 4 after the VGPRs; the total is
+    # allocated in granules
+    total = (-(-vgprs // 4) * 4 + agprs) if agprs else vgprs
+    return -(-total // GRANULE) * GRANULE
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC),
+                    reason="hipcc not available")
+def test_copy_wave_fits_beside_every_gemm_configuration():
+    copy = [v for k, v in _report(os.path.join(B.CSRC, "gemm_ag.hip")).items()
+            if "ag_copy_kernel" in k]
+    assert len(copy) == 1
+    copy_alloc = _alloc(copy[0]["VGPRs"], copy[0].get("AGPRs", 0))
+    assert copy[0].get("LDS", 0) == 0
+    gemms = {k: v for k, v in _report(os.path.join(B.CSRC, "gemm_bf16.hip")).items()
+             if "gemm_bf16_kernel" in k}
+    assert len(gemms) == 4
+    for name, r in gemms.items():
+        bm, bn, bk, stages, wgm, wgn = map(int, re.search(
+            r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups())
+        lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
+        wgs_per_cu = LDS_PER_CU // lds
+        waves_by_lds = -(-wgs_per_cu * wgm * wgn // SIMDS_PER_CU)
+        waves = min(r["Occupancy"], waves_by_lds)
+        gemm_alloc = _alloc(r["VGPRs"], r.get("AGPRs", 0))
+        free = VGPRS_PER_SIMD_LANE - waves * gemm_alloc
+        assert copy_alloc <= free, (bm, bn, waves, gemm_alloc, copy_alloc)
