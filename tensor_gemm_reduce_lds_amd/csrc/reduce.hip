@@ -207,8 +207,11 @@ __device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32
     return true;
 }
 
-// One-stage reduce: flags -> out.
-template <int WT, bool OUT_BF16, bool SB>
+// One-stage reduce: flags -> out.  ROWS2: two rows per thread and
+// iteration (2*W loads in flight); without it one row (W loads, fewer
+// registers: the slices that run beside the GEMM must fit in the registers
+// its workgroups leave free).  Both sum in the same order.
+template <int WT, bool OUT_BF16, bool SB, bool ROWS2 = true>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const TileGeom &g = a.g;
     const int32_t U = a.units_per_tile;
@@ -237,6 +240,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const int c4 = threadIdx.x % C4;
     const int64_t col = (int64_t)tn * g.BN + c4 * 4;
     const int64_t stride = g.Mc * g.N;
+    if constexpr (!ROWS2) {
+        for (int64_t row = lo + threadIdx.x / C4; row < hi; row += RPP) {
+            const int64_t d = row / g.Mc;
+            const int64_t idx = ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
+            store_out4(a.out, row * g.N + col, ordered_sum<WT, SB>(a.staging, idx, stride, W, L),
+                       OUT_BF16);
+        }
+        return;
+    }
     // two rows per thread per iteration: 2*W independent 16-byte loads
     for (int64_t row = lo + threadIdx.x / C4; row < hi; row += 2 * RPP) {
         const int64_t row2 = row + RPP;
@@ -344,6 +356,18 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     trace[b] = t;
 }
 
+template <bool BF, bool SB, bool ROWS2>
+hipError_t launch_w(const ReduceArgs &a, dim3 grid, hipStream_t s) {
+    switch (a.g.W) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<0, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool BF, bool SB>
 hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
     const int64_t units =
@@ -352,14 +376,9 @@ hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
                                        : (int64_t)a.g.T * a.units_per_tile;
     if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)units);
-    switch (a.g.W) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((reduce_kernel<0, BF, SB>), grid, dim3(kThreads), 0, s, a); break;
-    }
-    return hipGetLastError();
+    // slices run beside GEMM launches: the one-row form
+    if (a.slice_kind != kSliceAll) return launch_w<BF, SB, false>(a, grid, s);
+    return launch_w<BF, SB, true>(a, grid, s);
 }
 
 }  // namespace

@@ -66,3 +66,26 @@ def test_copy_wave_fits_beside_every_gemm_configuration():
         gemm_alloc = _alloc(r["VGPRs"], r.get("AGPRs", 0))
         free = VGPRS_PER_SIMD_LANE - waves * gemm_alloc
         assert copy_alloc <= free, (bm, bn, waves, gemm_alloc, copy_alloc)
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC),
+                    reason="hipcc not available")
+def test_overlap_reduce_slices_fit_beside_every_gemm_configuration():
+    """The overlapped reduce launches its slices (the one-row instantiations)
+    while GEMM workgroups hold the CUs; a slice wave that does not fit
+    beside them waits for them to retire and the overlap is lost (a
+    throughput property: the slices never wait on anything a GEMM
+    workgroup waits for)."""
+    red = {k: v for k, v in _report(os.path.join(B.CSRC, "reduce.hip")).items()
+           if "reduce_kernel" in k and k.endswith("ELb0EEEvNS_10ReduceArgsE")}
+    assert red, "one-row reduce instantiations not found"
+    need = max(_alloc(v["VGPRs"], v.get("AGPRs", 0)) for v in red.values())
+    gemms = {k: v for k, v in _report(os.path.join(B.CSRC, "gemm_bf16.hip")).items()
+             if "gemm_bf16_kernel" in k}
+    for name, r in gemms.items():
+        bm, bn, bk, stages, wgm, wgn = map(int, re.search(
+            r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups())
+        lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
+        waves = min(r["Occupancy"], -(-(LDS_PER_CU // lds) * wgm * wgn // SIMDS_PER_CU))
+        free = VGPRS_PER_SIMD_LANE - waves * _alloc(r["VGPRs"], r.get("AGPRs", 0))
+        assert need <= free, (bm, bn, need, free)
