@@ -286,6 +286,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int ST_PER_WAVE = SROWS / (NW * RPI);
     static_assert(SROWS * EP_PITCH <= STAGES * STAGE, "stripe fits in the stage buffers");
     static_assert(ST_PER_WAVE * NW * RPI == SROWS, "stripe rows split evenly");
+    static_assert(32 % (ST_PER_WAVE * RPI) == 0, "a wave's stripe rows stay in one 32-row group");
     const uint16_t *Cp = (const uint16_t *)a.C;
     const float alpha = a.alpha, beta = a.beta;
     const int h4 = 4 * (lane >> 5);
@@ -333,14 +334,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                     asm volatile("" : "+v"(cb_full[k].x), "+v"(cb_full[k].y));
             }
             __syncthreads();
+            // this lane's rows in the stripe are rowF + k*RPI (one 32-row
+            // group per wave), so the destination offset is computed once
+            // and advanced by RPI rows per store; only a row that crosses
+            // into the next chunk recomputes it
+            const int sr0 = wave * ST_PER_WAVE * RPI + srow;
+            const int64_t rowF = row0 + (sr0 >> 5) * WM + i * 32 + (sr0 & 31);
+            const int32_t dF = (int32_t)((uint64_t)rowF / (uint64_t)g.Mc);
+            const int64_t next_chunk = (int64_t)(dF + 1) * g.Mc;
+            const int64_t offF =
+                a.plain_out ? ((int64_t)r * g.M + rowF) * g.N + col0 + scol
+                            : (((int64_t)dF * g.W + r) * g.Mc + (rowF - (int64_t)dF * g.Mc)) * g.N +
+                                  col0 + scol;
 #pragma unroll
             for (int k = 0; k < ST_PER_WAVE; ++k) {
-                const int sr = (wave * ST_PER_WAVE + k) * RPI + srow;   // row in the stripe set
-                const int64_t row = row0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+                const int sr = sr0 + k * RPI;               // row in the stripe set
+                const int64_t row = rowF + k * RPI;
                 f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
                     smem + sr * EP_PITCH + scol * 4);
                 if (row < g.M) {
-                    const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
+                    int32_t d = dF;
+                    int64_t off = offF + (int64_t)(k * RPI) * g.N;
+                    if (row >= next_chunk) {                 // a chunk boundary inside the group
+                        d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
+                        off = a.plain_out
+                                  ? ((int64_t)r * g.M + row) * g.N + col0 + scol
+                                  : (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) *
+                                            g.N + col0 + scol;
+                    }
                     if constexpr (MODE != 0) {
                         const uint2 cb = MODE == 1 ? cb_row : cb_full[k];
                         const float y0 = x[0] + beta * __uint_as_float(cb.x << 16);
@@ -353,11 +374,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         x[2] = own ? y2 : x[2];
                         x[3] = own ? y3 : x[3];
                     }
-                    const int64_t off =
-                        a.plain_out
-                            ? ((int64_t)r * g.M + row) * g.N + col0 + scol
-                            : (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N +
-                                  col0 + scol;
                     // whole 128-byte lines from one instruction: a streaming
                     // store keeps the staging from evicting the A/B panels
                     // other tiles are still reading
