@@ -51,6 +51,13 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
                  :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// A workgroup barrier for LDS hand-offs only: it waits for this wave's LDS
+// operations but not for its global stores, which __syncthreads would also
+// drain (its release fence covers global memory), a full memory latency.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -300,9 +307,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     auto epilogue = [&](auto mode_tag) {
         constexpr int MODE = decltype(mode_tag)::value;
         uint2 cb_row = {0u, 0u};
+        float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // the bias row's 4 columns, widened
         if constexpr (MODE == 1) {
             cb_row = *(const uint2 *)(Cp + col0 + scol);
             asm volatile("" : "+v"(cb_row.x), "+v"(cb_row.y));   // wait here, once
+            cf[0] = __uint_as_float(cb_row.x << 16);
+            cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
+            cf[2] = __uint_as_float(cb_row.y << 16);
+            cf[3] = __uint_as_float(cb_row.y & 0xffff0000u);
         }
         __syncthreads();                            // every wave is done with the stages
 #pragma unroll
@@ -333,7 +345,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                 for (int k = 0; k < ST_PER_WAVE; ++k)   // one wait, before any store
                     asm volatile("" : "+v"(cb_full[k].x), "+v"(cb_full[k].y));
             }
-            __syncthreads();
+            lds_barrier();                          // the stripe is in LDS
             // this lane's rows in the stripe are rowF + k*RPI (one 32-row
             // group per wave), so the destination offset is computed once
             // and advanced by RPI rows per store; only a row that crosses
@@ -346,6 +358,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                 a.plain_out ? ((int64_t)r * g.M + rowF) * g.N + col0 + scol
                             : (((int64_t)dF * g.W + r) * g.Mc + (rowF - (int64_t)dF * g.Mc)) * g.N +
                                   col0 + scol;
+            auto store_rows = [&] {
 #pragma unroll
             for (int k = 0; k < ST_PER_WAVE; ++k) {
                 const int sr = sr0 + k * RPI;               // row in the stripe set
@@ -392,7 +405,53 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                     }
                 }
             }
-            if (i + 1 < FM) __syncthreads();        // the stripe buffer is reused
+            };
+            const int64_t rowL = rowF + (int64_t)(ST_PER_WAVE - 1) * RPI;
+            if constexpr (MODE != 2) {
+                if (rowL < g.M && rowL < next_chunk) {
+                    // the common case: every row of the group lies inside the
+                    // matrix and in one chunk, so the owner test, the C term
+                    // and the staging format are decided once, and each row
+                    // is one LDS read, an optional add and one store
+                    const bool add_c = MODE == 1 && dF == r;
+                    const int64_t step = (int64_t)RPI * g.N;
+                    if (a.staging_bf16) {
+                        uint16_t *dst = (uint16_t *)a.staging + offF;
+#pragma unroll
+                        for (int k = 0; k < ST_PER_WAVE; ++k, dst += step) {
+                            f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
+                                smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
+                            if (add_c)
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
+                            const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
+                            const __bf16 h2 = (__bf16)x[2], h3 = (__bf16)x[3];
+                            u32x2_t hw;
+                            hw[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                            hw[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                            __builtin_nontemporal_store(hw, (u32x2_t *)dst);
+                        }
+                    } else {
+                        float *dst = (float *)a.staging + offF;
+#pragma unroll
+                        for (int k = 0; k < ST_PER_WAVE; ++k, dst += step) {
+                            f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
+                                smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
+                            if (add_c)
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
+                            __builtin_nontemporal_store(x, (f32x4_t *)dst);
+                        }
+                    }
+                } else {
+                    store_rows();   // ragged rows or a chunk boundary inside the group
+                }
+            } else {
+                store_rows();
+            }
+            if (i + 1 < FM) lds_barrier();          // the stripe buffer is reused
         }
     };
     if (!a.has_c) epilogue(std::integral_constant<int, 0>{});
@@ -413,7 +472,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        __syncthreads();
+        // the consumer runs after this kernel has completed, so the flag
+        // needs no ordering against the other waves' stores here
         if (tid == 0)
             __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
