@@ -292,6 +292,10 @@ int gemm_ag_run(gemm_ag_plan_t p, const void *X, const void *B, void *out, void 
     a.b_offset = 0;
     a.n_blocks = (uint32_t)(p->g.W * p->g.T);
     a.plain_out = 1;
+    // fused: tiles run rank-interleaved, the order the copies deliver
+    // tile-rows in; otherwise every tile-row is already there and the
+    // XCD map of the reduce-scatter GEMM applies
+    a.xcd_rank_major = (do_copy && (run_flags & GEMM_AG_FUSED)) ? 0 : 1;
     a.signals = p->signals;
     a.epoch = wait_epoch;
     a.timeout_ticks = p->timeout_ticks;
