@@ -92,6 +92,12 @@ typedef struct gemm_ag_info {
 GEMM_RS_API int gemm_ag_plan(const gemm_ag_desc_t *desc, gemm_ag_plan_t *out_plan);
 
 /*
+ * Device: a plan belongs to the device that was current at gemm_ag_plan;
+ * gemm_ag_run and gemm_ag_status return INVALID_ARG unless that device is
+ * current; gemm_ag_destroy switches to it by itself.
+ */
+
+/*
  * gemm_ag_run: enqueue one pass on `stream`, no host synchronisation.
  *   X    [W][M/W][K] bfloat16 row shards, 16-byte aligned     (RUN_COPY)
  *   B    [W][K][N]   bfloat16, row-major, 16-byte aligned     (RUN_GEMM)

@@ -168,6 +168,13 @@ typedef struct gemm_rs_info {
 GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
 
 /*
+ * Device: a plan belongs to the device that was current at gemm_rs_plan.
+ * gemm_rs_run, gemm_rs_tile_order and gemm_rs_status must be called with
+ * that device current (they return INVALID_ARG otherwise, before enqueuing
+ * anything); gemm_rs_destroy switches to it by itself.
+ */
+
+/*
  * gemm_rs_run: enqueue one pass on `stream`, with no host synchronisation
  * and no memset.
  *   A    [W][M][K] row-major (dtype), 16-byte aligned     (RUN_GEMM)

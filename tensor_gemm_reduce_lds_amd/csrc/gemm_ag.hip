@@ -183,6 +183,12 @@ int validate_ag(const gemm_ag_desc_t &d, int32_t bm, int32_t bn) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// work is only enqueued while the plan's device is current
+bool on_plan_device(int device) {
+    int cur = -1;
+    return hipGetDevice(&cur) == hipSuccess && cur == device;
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,7 +254,7 @@ int gemm_ag_plan(const gemm_ag_desc_t *desc, gemm_ag_plan_t *out) {
 
 int gemm_ag_run(gemm_ag_plan_t p, const void *X, const void *B, void *out, void *stream,
                 uint32_t run_flags) {
-    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     const uint32_t known = GEMM_AG_RUN_COPY | GEMM_AG_RUN_GEMM | GEMM_AG_FUSED |
                            GEMM_AG_EXPECT_NEXT;
     if (run_flags & ~known) return GEMM_RS_ERR_INVALID_ARG;
@@ -333,7 +339,7 @@ int gemm_ag_query(gemm_ag_plan_t p, gemm_ag_info_t *info) {
 }
 
 int gemm_ag_status(gemm_ag_plan_t p, void *stream, int32_t *detail) {
-    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize(p->copy);
     int32_t h[4] = {0, 0, 0, 0};

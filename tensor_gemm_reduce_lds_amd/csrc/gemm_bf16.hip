@@ -27,6 +27,7 @@
 // sm80 gemm+rs", section "cutlass自定义epilogue–sm80": a compute node
 // alpha*acc + beta*C, a store node that scatters by destination, and a
 // per-tile flag).
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_rs_internal.h"
@@ -485,14 +486,20 @@ template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
     constexpr size_t lds_bytes = (size_t)STAGES * (BM + BN) * BK * 2;
     static_assert(lds_bytes <= 160 * 1024, "LDS");
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(
+    // the dynamic LDS limit is a per-device attribute of the kernel: set it
+    // once per device (thread-safe)
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t set_rc[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
+        set_rc[dev] = hipFuncSetAttribute(
             (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    });
+    if (set_rc[dev] != hipSuccess) return set_rc[dev];
     const int64_t blocks = a.n_blocks;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>),
                        dim3((unsigned)blocks), dim3(64 * WGM * WGN), lds_bytes, s, a);

@@ -137,6 +137,13 @@ void free_plan(gemm_rs_plan_s *p) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The plan's memory lives on one device: work is only enqueued while that
+// device is current (its pointers mean nothing on another device).
+bool on_plan_device(int device) {
+    int cur = -1;
+    return hipGetDevice(&cur) == hipSuccess && cur == device;
+}
+
 // Zero every flag, counter and the error word (plan time and after errors).
 hipError_t clear_protocol_state(gemm_rs_plan_s *p, hipStream_t s) {
     hipError_t e = hipMemsetAsync(p->flags, 0, p->flags_bytes, s);
@@ -278,7 +285,7 @@ int gemm_rs_query(gemm_rs_plan_t p, gemm_rs_info_t *info) {
 int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
                 float alpha, float beta, void *out, void *stream,
                 uint32_t run_flags) {
-    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     const uint32_t known = GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE |
                            GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES |
                            GEMM_RS_OVERLAP_REDUCE;
@@ -403,7 +410,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
 }
 
 int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {
-    if (!p || !host_trace) return GEMM_RS_ERR_INVALID_ARG;
+    if (!p || !host_trace || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     hipError_t e = launch_tile_order(p->g, p->trace, nullptr);
     if (e == hipSuccess)
         e = hipMemcpy(host_trace, p->trace, p->trace_bytes, hipMemcpyDeviceToHost);
@@ -411,7 +418,7 @@ int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {
 }
 
 int gemm_rs_status(gemm_rs_plan_t p, void *stream, int32_t *detail) {
-    if (!p) return GEMM_RS_ERR_INVALID_ARG;
+    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     int32_t e4[4] = {0, 0, 0, 0};
     if (hipStreamSynchronize(s) != hipSuccess) return GEMM_RS_ERR_HIP;
