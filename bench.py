@@ -98,11 +98,110 @@ def cpu_baseline(w, x, budget_s: float):
         t += time.perf_counter() - t1
         rows += more
     flops = rows * w.W * 2 * w.N * w.K
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": "fp64 reference of output rows [0, %d) of %d (all %d ranks, "
                       "K=%d, N=%d): %.3g GFLOP in %.1f s" % (
                           rows, w.M, w.W, w.K, w.N, flops / 1e9, t)}
+
+
+def ablation_measure(plan, A, B, C, out, w, stream, steps):
+    """The pages' ablation modes and reference points, reported beside the
+    headline (none is a target).  kernel-sync: every step followed by a
+    stream synchronisation.  clear-kernel: the staging buffer cleared before
+    every step, the memset a design that accumulates in place would need
+    (this one stores per-source slots and never clears).  Cold reduce: the
+    GEMM alone, then a 512 MiB write that flushes the memory-side cache,
+    then the reduce alone.  Context: torch.bmm (hipBLASLt) on the same W
+    GEMMs with a bfloat16 output and no scatter; the library never calls it."""
+    import ctypes
+    import statistics
+    import torch
+    from tensor_gemm_reduce_lds_amd import gemm_rs as G
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemsetAsync.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+    hip.hipMemsetAsync.restype = ctypes.c_int
+    n = max(5, steps // 2)
+    info = plan.info
+
+    def run(flags=G.RUN_ALL):
+        plan.run(A, B, C, w.alpha, w.beta, out, stream, flags)
+
+    def check(what):
+        rc, detail = plan.status(stream)
+        if rc != G.OK:
+            raise RuntimeError("%s failed: %s %s" % (what, G.gemm_rs_strerror(rc), detail))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        run()
+        stream.synchronize()
+    sync_ms = (time.perf_counter() - t0) * 1e3 / n
+    check("kernel-sync")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        if hip.hipMemsetAsync(info.staging, 0, info.staging_bytes, stream.cuda_stream) != 0:
+            raise RuntimeError("hipMemsetAsync failed")
+        run()
+    torch.cuda.synchronize()
+    clear_ms = (time.perf_counter() - t0) * 1e3 / n
+    check("clear-kernel")
+
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=out.device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cold = []
+    for _ in range(n):
+        run(G.RUN_GEMM)
+        flush.fill_(1.0)
+        e0.record(stream)
+        run(G.RUN_REDUCE)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    check("cold reduce")
+    del flush
+    cold_ms = statistics.median(cold)
+    _, red_bytes = algorithmic_bytes(w, w.elem_bytes)
+    result = {
+        "kernel_sync_ms_per_step": round(sync_ms, 4),
+        "clear_kernel_ms_per_step": round(clear_ms, 4),
+        "clear_bytes": int(info.staging_bytes),
+        "cold_reduce_ms": round(cold_ms, 4),
+        "cold_reduce_gbps": round(red_bytes / (cold_ms * 1e-3) / 1e9, 1),
+    }
+    if w.dtype == "bf16":
+        Ab = A.view(torch.bfloat16)
+        Bb = B.view(torch.bfloat16).contiguous()
+        Cb = torch.empty((w.W, w.M, w.N), dtype=torch.bfloat16, device=out.device)
+        for _ in range(2):
+            torch.bmm(Ab, Bb, out=Cb)
+        e0.record(stream)
+        for _ in range(n):
+            torch.bmm(Ab, Bb, out=Cb)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bmm_ms = e0.elapsed_time(e1) / n
+        result["torch_bmm_ms"] = round(bmm_ms, 4)
+        result["torch_bmm_tflops"] = round(w.flops / (bmm_ms * 1e-3) / 1e12, 2)
+        del Cb
+    result["note"] = ("ablations and context, not targets: kernel-sync and clear-kernel are "
+                      "whole steps; torch_bmm is hipBLASLt on the same GEMMs without the "
+                      "scatter epilogue or the reduce")
+    return result
 
 
 def ag_measure(steps, stream):
@@ -319,6 +418,10 @@ def main():
                         "its own accuracy bar), not the headline configuration",
             }
 
+    ablation = None
+    if not args.no_overlap:
+        ablation = ablation_measure(plan, A, B, C, out, w, stream, args.steps)
+
     # all-gather fused into the GEMM prologue, on the up-projection shard of
     # the same layer (a second workload, reported beside the headline)
     ag_gemm = None
@@ -373,6 +476,7 @@ def main():
         "value_overlap_identity": (None if ov_id_ms is None
                                    else round(flops / (ov_id_ms * 1e-3) / 1e12, 2)),
         "bf16_staging": bf16_staging,
+        "ablation": ablation,
         "ag_gemm": ag_gemm,
     }
     plan.close()
