@@ -89,7 +89,9 @@ extern "C" {
  * a flat or two-level reduction order.
  *
  *   M, N, K      per-rank GEMM shape; M % W == 0 (rank d receives M/W rows);
- *                each below 2^31
+ *                each below 2^31; M, N >= 1.  K == 0 is allowed: the
+ *                empty sum, so every partial is 0 and out = beta*C
+ *                (A and B are then never read and may be NULL)
  *   W            virtual ranks, 1..64
  *   dtype        GEMM_RS_BF16 or GEMM_RS_F32
  *   tile_m/_n    output tile (the communication unit); 0 picks a default.
@@ -159,7 +161,8 @@ typedef struct gemm_rs_info {
  * the current HIP device (staging W*M*N*4 bytes, flags, counters, error
  * word, trace, optional sub-group buffers) and zero the flags once,
  * synchronously.  On success *out owns all of it until gemm_rs_destroy.
- * Returns OK, INVALID_ARG (NULL desc/out, W outside 1..64, M % W != 0,
+ * Returns OK, INVALID_ARG (NULL desc/out, W outside 1..64, M or N < 1,
+ * K < 0, M % W != 0,
  * unknown enum, bad ldc, materialize_sub without the two-level order),
  * UNSUPPORTED (tile not in the set above, N % tile_n != 0, K % 64 != 0,
  * ldc % 8 != 0, M, N or K of 2^31 or more, grid over 2^31-1) or HIP.  Invalid descriptors are

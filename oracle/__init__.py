@@ -72,7 +72,8 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
             swizzle, has_c, ldc, materialize_sub, staging_dtype)
     if any(not isinstance(v, (int, np.integer)) for v in ints):
         return INVALID_ARG
-    if W < 1 or W > MAX_W or M < 1 or N < 1 or K < 1:
+    # K == 0 is the empty sum: every partial is 0, so out = beta*C
+    if W < 1 or W > MAX_W or M < 1 or N < 1 or K < 0:
         return INVALID_ARG
     if M % W != 0:
         return INVALID_ARG

@@ -131,7 +131,8 @@ static void rank_row(int64_t M, int64_t N, int64_t K, int32_t W, int32_t dtype,
 static int check_shape(int64_t M, int64_t N, int64_t K, int32_t W,
                        int32_t order, int32_t groups)
 {
-    if (M <= 0 || N <= 0 || K <= 0 || W <= 0 || M % W != 0)
+    /* K == 0 is the empty sum: every partial is 0 */
+    if (M <= 0 || N <= 0 || K < 0 || W <= 0 || M % W != 0)
         return -1;
     if (order == OR_TWO_LEVEL && (groups <= 0 || W % groups != 0))
         return -1;

@@ -69,7 +69,8 @@ void pick_default_tile(const gemm_rs_desc_t &d, int32_t *bm, int32_t *bn) {
 
 // Problem-level checks: INVALID_ARG.  Implementation limits: UNSUPPORTED.
 int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
-    if (d.W < 1 || d.W > kMaxW || d.M < 1 || d.N < 1 || d.K < 1)
+    // K == 0 is the empty sum: every partial is 0 and out = beta*C
+    if (d.W < 1 || d.W > kMaxW || d.M < 1 || d.N < 1 || d.K < 0)
         return GEMM_RS_ERR_INVALID_ARG;
     if (d.M % d.W != 0) return GEMM_RS_ERR_INVALID_ARG;
     if (d.dtype != GEMM_RS_BF16 && d.dtype != GEMM_RS_F32)
@@ -293,7 +294,8 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     const bool do_gemm = run_flags & GEMM_RS_RUN_GEMM;
     const bool do_reduce = run_flags & GEMM_RS_RUN_REDUCE;
     if (do_gemm) {
-        if (!A || !B || !aligned16(A) || !aligned16(B))
+        // with K == 0 the operands are never read and may be NULL
+        if ((p->g.K > 0 && (!A || !B)) || !aligned16(A) || !aligned16(B))
             return GEMM_RS_ERR_INVALID_ARG;
         if (p->d.has_c && (!C || !aligned16(C))) return GEMM_RS_ERR_INVALID_ARG;
         if (!p->d.has_c && C) return GEMM_RS_ERR_INVALID_ARG;

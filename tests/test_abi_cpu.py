@@ -69,7 +69,7 @@ def test_strerror_and_null_handles():
 
 
 BAD = [
-    dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=0), dict(dtype=7),
+    dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=-64), dict(N=0), dict(dtype=7),
     dict(order=2), dict(order=1, groups=3), dict(order=1, groups=0), dict(swizzle=4),
     dict(swizzle=-1),
     dict(has_c=1, ldc=100), dict(has_c=2), dict(ldc=-8), dict(materialize_sub=1),

@@ -270,6 +270,40 @@ def test_edge_tile_orders_bit_exact():
                     (name, swz)
 
 
+@pytest.mark.parametrize("dtype,ldc", [("bf16", 0), ("bf16", 256), ("f32", 0)])
+def test_k0_empty_sum_is_beta_c(dtype, ldc):
+    """K = 0: the empty sum.  Every partial is 0, so the output is beta*C
+    (added once, by the chunk owner), bit for bit as the oracle's float
+    pipeline gives it; A and B are never read and are passed as NULL."""
+    import torch
+    base = W70["llama70b"] if dtype == "bf16" else W70["tiny_f32"]
+    w = I.with_shape(base, W=8, M=512, N=256, K=64, has_c=True, ldc=ldc,
+                     alpha=1.5, beta=0.75, c_std=1.0,
+                     tile_m=256 if dtype == "bf16" else 64,
+                     tile_n=256 if dtype == "bf16" else 64)
+    x = I.make_inputs(w)
+    C = x["C"]
+    A0 = x["A"][:, :, :0]
+    B0 = x["B"][:, :0, :]
+    say("k0", dtype, ldc)
+    Cd = torch.from_numpy(C.view(np.int16) if C.dtype == np.uint16 else C).to("cuda:0")
+    with G.Plan(**desc_fields(w, K=0)) as plan:
+        out = new_out(w)
+        s = torch.cuda.current_stream()
+        plan.run(None, None, Cd, w.alpha, w.beta, out, s)
+        rc, detail = plan.status(s)
+        assert rc == G.OK, (rc, detail)
+        assert not flags(plan).any()
+        bits = out_bits(out)
+    kw = oracle_kw(w)
+    want = O.emulate_rows(A0, B0, C, **kw)
+    assert np.array_equal(bits, want.view(bits.dtype))
+    ref = O.reference_rows(A0, B0, C, **kw)
+    Cf = O.bf16_bits_to_f64(C) if dtype == "bf16" else C.astype(np.float64)
+    np.testing.assert_array_equal(ref, 0.75 * (np.broadcast_to(Cf, (w.M, w.N)) if ldc == 0
+                                               else Cf[:, :w.N]))
+
+
 @pytest.mark.parametrize("tile", [(256, 128), (128, 128)])
 def test_llama70b_other_tiles_sampled(tile):
     """The 70B-like shard with the smaller tile shapes (sampled elements)."""

@@ -167,6 +167,31 @@ def test_alpha0_beta1_returns_c_bits():
     assert np.array_equal(got, np.broadcast_to(C, (M, N)))
 
 
+@pytest.mark.parametrize("ldc", [0, 16])
+def test_k0_empty_sum_is_beta_c(ldc):
+    """K = 0: every partial product is the empty sum 0, so the output is
+    beta*C, counted once (closed form), and in the float pipeline the
+    bfloat16 rounding of the float beta*C (other ranks add exact zeros)."""
+    rng = np.random.default_rng(9)
+    W, M, N = 4, 8, 16
+    A = np.zeros((W, M, 0), dtype=np.uint16)
+    B = np.zeros((W, 0, N), dtype=np.uint16)
+    C = I.to_bf16_bits(rng.standard_normal((N,) if ldc == 0 else (M, ldc)).astype(np.float32))
+    Cf = O.bf16_bits_to_f64(C)
+    Cm = np.broadcast_to(Cf, (M, N)) if ldc == 0 else Cf[:, :N]
+    beta = 0.75
+    ref = O.reference_rows(A, B, C, dtype=O.BF16, alpha=1.5, beta=beta, ldc=ldc)
+    np.testing.assert_array_equal(ref, beta * Cm)
+    for order, groups in ((O.FLAT, 1), (O.TWO_LEVEL, 2)):
+        got = O.emulate_rows(A, B, C, dtype=O.BF16, alpha=1.5, beta=beta, ldc=ldc,
+                             order=order, groups=groups)
+        want = O.bf16_rne((beta * Cm).astype(np.float32)).reshape(M, N)
+        assert np.array_equal(got, want)
+    # no C: all zeros
+    z = O.reference_rows(A, B, None, dtype=O.BF16, alpha=1.5)
+    assert not z.any()
+
+
 # ------------------------------------------------------------ reduce order
 def _order_case(dtype):
     # rank r's partial at every element is v[r]: A_r = v[r] (K = 1), B_r = 1
@@ -427,6 +452,9 @@ TILES = [(256, 256), (64, 64)]
     (dict(W=65), O.INVALID_ARG),
     (dict(M=1000, W=3), O.INVALID_ARG),
     (dict(M=0), O.INVALID_ARG),
+    (dict(N=0), O.INVALID_ARG),
+    (dict(K=-64), O.INVALID_ARG),
+    (dict(K=0), O.OK),
     (dict(dtype=7), O.INVALID_ARG),
     (dict(order=2), O.INVALID_ARG),
     (dict(order=O.TWO_LEVEL, groups=3), O.INVALID_ARG),
