@@ -107,7 +107,28 @@ def cpu_baseline(w, x, budget_s: float):
                     break
     except OSError:
         pass
+    # single-thread oracle times on the two small configurations: the whole
+    # fp32 tiny case, and the first rows of the m <= 64 decode shard
+    from tensor_gemm_reduce_lds_amd import inputs as I
+    single = {}
+    O.set_threads(1)
+    try:
+        for name, n_rows in (("tiny_f32", None), ("decode", 8)):
+            ws = I.WORKLOADS[name]
+            xs = I.make_inputs(ws)
+            kws = dict(dtype=O.BF16 if ws.dtype == "bf16" else O.F32, alpha=ws.alpha,
+                       beta=ws.beta, ldc=ws.ldc)
+            hi = ws.M if n_rows is None else n_rows
+            t1 = time.perf_counter()
+            O.reference_rows(xs["A"], xs["B"], xs["C"], row_lo=0, row_hi=hi, **kws)
+            ts = time.perf_counter() - t1
+            fl = hi * ws.W * 2 * ws.N * ws.K
+            single[name] = {"rows": hi, "of_rows": ws.M, "seconds": round(ts, 4),
+                            "gflops": round(fl / ts / 1e9, 3)}
+    finally:
+        O.set_threads(threads)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "single_thread": single,
             "kind": "oracle", "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": "fp64 reference of output rows [0, %d) of %d (all %d ranks, "
@@ -428,8 +449,10 @@ def main():
     if not args.no_overlap and w.name == "llama70b":
         ag_gemm = ag_measure(args.steps, stream)
 
-    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    gemm_list = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    red_list = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    gemm_ms = sum(gemm_list) / args.steps
+    red_ms = sum(red_list) / args.steps
     step_ms = wall * 1e3 / args.steps
     flops = w.flops
     elem = w.elem_bytes
@@ -463,10 +486,14 @@ def main():
                      "frac": round(gemm_tflops / peak, 4),
                      "traffic": traffic},
         "gemm_kernel_ms": round(gemm_ms, 4),
+        "gemm_kernel_ms_median": round(gemm_list[len(gemm_list) // 2], 4),
+        "gemm_kernel_ms_min": round(gemm_list[0], 4),
         "gemm_tflops": round(gemm_tflops, 2),
         "mfma_util_pct": round(100 * gemm_tflops / peak, 2),
         "gemm_algorithmic_bytes": gemm_bytes,
         "reduce_kernel_ms": round(red_ms, 4),
+        "reduce_kernel_ms_median": round(red_list[len(red_list) // 2], 4),
+        "reduce_kernel_ms_min": round(red_list[0], 4),
         "reduce_gbps": round(red_gbps, 1),
         "reduce_hbm_frac": round(red_gbps / PEAK_HBM_GBPS, 4),
         "reduce_algorithmic_bytes": red_bytes,

@@ -293,6 +293,8 @@ def _load():
     lib.oracle_bf16_rne_array.argtypes = [i64, vp, vp]
     lib.oracle_bf16_rne_array.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     for f in (lib.oracle_partial_rows, lib.oracle_reference_rows,
               lib.oracle_emulate_rows, lib.oracle_reference_elems,
               lib.oracle_reduce_emulate):
@@ -303,6 +305,11 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the oracle's next calls (timing only)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _ptr(a):

@@ -87,6 +87,17 @@ void oracle_bf16_rne_array(int64_t n, const float *x, uint16_t *out)
         out[i] = oracle_bf16_rne(x[i]);
 }
 
+/* Threads the next parallel region may use (timing a single-thread baseline). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
