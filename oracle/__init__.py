@@ -53,7 +53,7 @@ _lib = None
 def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
              groups=1, swizzle=REMOTE_FIRST, has_c=0, ldc=0,
              materialize_sub=0, supported_tiles: Optional[Sequence] = None,
-             staging_dtype=STAGING_F32):
+             staging_dtype=STAGING_F32, interleave=0):
     """Return the status a plan must give for this descriptor.
 
     INVALID_ARG: the problem itself is ill-posed.  A reduce-scatter over W
@@ -69,7 +69,7 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     float32 inputs or with the materialised two-level buffers.
     """
     ints = (M, N, K, W, dtype, tile_m, tile_n, group_m, order, groups,
-            swizzle, has_c, ldc, materialize_sub, staging_dtype)
+            swizzle, has_c, ldc, materialize_sub, staging_dtype, interleave)
     if any(not isinstance(v, (int, np.integer)) for v in ints):
         return INVALID_ARG
     # K == 0 is the empty sum: every partial is 0, so out = beta*C
@@ -86,6 +86,10 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     if order == TWO_LEVEL and (groups < 1 or W % groups != 0):
         return INVALID_ARG
     if swizzle not in (REMOTE_FIRST, SELF_FIRST, IDENTITY, TILE_INTERLEAVED):
+        return INVALID_ARG
+    # tiles per destination visit: 0 or 1 is one tile; more only means
+    # something for the tile-interleaved order
+    if interleave < 0 or (interleave > 1 and swizzle != TILE_INTERLEAVED):
         return INVALID_ARG
     if has_c not in (0, 1) or ldc < 0 or (has_c and ldc != 0 and ldc < N):
         return INVALID_ARG
@@ -127,11 +131,12 @@ class Geometry:
     """
 
     def __init__(self, M, N, K, W, tile_m, tile_n, group_m=1,
-                 swizzle=REMOTE_FIRST, order=FLAT, groups=1):
+                 swizzle=REMOTE_FIRST, order=FLAT, groups=1, interleave=1):
         self.M, self.N, self.K, self.W = M, N, K, W
         self.BM, self.BN = tile_m, tile_n
         self.g = max(1, group_m)
         self.swizzle = swizzle
+        self.q = max(1, interleave)
         self.order, self.groups = order, (groups if order == TWO_LEVEL else 1)
         self.Mc = M // W
         self.tiles_m = -(-M // tile_m)
@@ -219,19 +224,23 @@ class Geometry:
         TILE_INTERLEAVED (a reading of the tile-interleaved variant of the
         remote-first order: every destination in flight at once instead of
         one chunk per step): rank r visits the destinations dest(r, 0..W-1)
-        in turn and takes the next tile of each on every visit; a chunk
-        whose tiles are used up is skipped."""
+        in turn and takes the next q = ``interleave`` tiles of each on every
+        visit (round j takes the chunk's tiles [j*q, (j+1)*q)); a chunk with
+        fewer left gives what remains, a used-up chunk is skipped.  q = 1 is
+        one tile per visit; q at least the largest chunk's tile count is the
+        chunk-major remote-first order."""
         if self.swizzle != TILE_INTERLEAVED:
             out = []
             for s in range(self.W):
                 out.extend(self.chunk_tiles(self.dest(r, s)))
             return out
         lists = [self.chunk_tiles(self.dest(r, s)) for s in range(self.W)]
+        q = self.q
+        rounds = -(-max(len(x) for x in lists) // q)
         out = []
-        for j in range(max(len(x) for x in lists)):
+        for j in range(rounds):
             for s in range(self.W):
-                if j < len(lists[s]):
-                    out.append(lists[s][j])
+                out.extend(lists[s][j * q:(j + 1) * q])
         return out
 
     def seq_table(self) -> np.ndarray:

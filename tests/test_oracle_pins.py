@@ -359,6 +359,52 @@ def test_tile_interleaved_properties(g):
                 assert sorted(G.owner(t // G.tiles_n) for t in tab[:, k]) == list(range(W))
 
 
+def test_tile_interleaved_blocks_hand_examples():
+    # W=2, one tile-row per chunk, 4 tile-columns: chunk 0 = [0, 1, 2, 3],
+    # chunk 1 = [4, 5, 6, 7].  Rank 0 visits chunk 1 then chunk 0, rank 1
+    # chunk 0 then chunk 1, taking q tiles per visit.
+    G = O.Geometry(4, 8, 64, 2, 2, 2, swizzle=O.TILE_INTERLEAVED, interleave=2)
+    assert [G.chunk_tiles(d) for d in range(2)] == [[0, 1, 2, 3], [4, 5, 6, 7]]
+    assert G.seq(0) == [4, 5, 0, 1, 6, 7, 2, 3]
+    assert G.seq(1) == [0, 1, 4, 5, 2, 3, 6, 7]
+    assert G.trace().tolist() == [4, 0, 5, 1, 0, 4, 1, 5, 6, 2, 7, 3, 2, 6, 3, 7]
+    # q = 3: the second round has one tile left in each chunk
+    G = O.Geometry(4, 8, 64, 2, 2, 2, swizzle=O.TILE_INTERLEAVED, interleave=3)
+    assert G.seq(0) == [4, 5, 6, 0, 1, 2, 7, 3]
+    assert G.seq(1) == [0, 1, 2, 4, 5, 6, 3, 7]
+    # unequal chunks [0, 1] and [2] with q = 2
+    G = O.Geometry(6, 16, 64, 2, 2, 16, swizzle=O.TILE_INTERLEAVED, interleave=2)
+    assert G.seq(0) == [2, 0, 1]
+    assert G.seq(1) == [0, 1, 2]
+
+
+@pytest.mark.parametrize("q", [1, 2, 3, 16])
+def test_tile_interleaved_blocks_properties(q):
+    """Every order is a permutation that keeps each chunk's own order; with
+    equal chunks of a multiple of q tiles, rank r's k-th tile lies in chunk
+    (r + 1 + k // q) mod W; q of at least the largest chunk is the
+    chunk-major remote-first order; q = 1 is one tile per visit."""
+    for (M, N, K, W, bm, bn) in _geom_cases() + _random_geoms():
+        for g in (1, 3):
+            G = O.Geometry(M, N, K, W, bm, bn, group_m=g, swizzle=O.TILE_INTERLEAVED,
+                           interleave=q)
+            tab = G.seq_table()
+            counts = [len(G.chunk_tiles(d)) for d in range(W)]
+            for r in range(W):
+                assert sorted(tab[r].tolist()) == list(range(G.T))
+                for d in range(W):
+                    mine = [t for t in tab[r] if G.owner(t // G.tiles_n) == d]
+                    assert mine == G.chunk_tiles(d)
+            if len(set(counts)) == 1 and counts[0] % q == 0:
+                for r in range(W):
+                    for k in range(G.T):
+                        assert G.owner(tab[r, k] // G.tiles_n) == (r + 1 + k // q) % W
+            big = O.Geometry(M, N, K, W, bm, bn, group_m=g, swizzle=O.TILE_INTERLEAVED,
+                             interleave=max(counts))
+            rf = O.Geometry(M, N, K, W, bm, bn, group_m=g, swizzle=O.REMOTE_FIRST)
+            assert np.array_equal(big.seq_table(), rf.seq_table())
+
+
 def test_identity_swizzle_same_order_everywhere():
     G = O.Geometry(8 * 512, 1024, 64, 8, 256, 256, swizzle=O.IDENTITY)
     tab = G.seq_table()
@@ -472,6 +518,10 @@ TILES = [(256, 256), (64, 64)]
     (dict(N=1000), O.UNSUPPORTED),
     (dict(K=100), O.UNSUPPORTED),
     (dict(swizzle=O.TILE_INTERLEAVED), O.OK),
+    (dict(swizzle=O.TILE_INTERLEAVED, interleave=32), O.OK),
+    (dict(interleave=1), O.OK),
+    (dict(interleave=2), O.INVALID_ARG),
+    (dict(swizzle=O.TILE_INTERLEAVED, interleave=-1), O.INVALID_ARG),
     (dict(staging_dtype=O.STAGING_BF16), O.OK),
     (dict(staging_dtype=2), O.INVALID_ARG),
     (dict(staging_dtype=O.STAGING_BF16, dtype=O.F32, tile_m=64, tile_n=64), O.UNSUPPORTED),
