@@ -66,9 +66,10 @@ extern "C" {
 #define GEMM_RS_SWIZZLE_SELF_FIRST   1 /* dest(r,s) = (r+s) mod W             */
 #define GEMM_RS_SWIZZLE_IDENTITY     2 /* dest(r,s) = s (no swizzle)          */
 #define GEMM_RS_SWIZZLE_TILE_INTERLEAVED 3 /* dest(r,s) = (r+1+s) mod W, visited
-                                              one tile at a time: rank r's k-th
-                                              tile goes to dest(r, k mod W)
-                                              while every chunk has tiles left */
+                                              q = interleave tiles at a time:
+                                              rank r's k-th tile goes to
+                                              dest(r, (k/q) mod W) while every
+                                              chunk has tiles left */
 
 /* staging element type (gemm_rs_desc_t.staging_dtype) */
 #define GEMM_RS_STAGING_F32  0
@@ -113,6 +114,11 @@ extern "C" {
  *                (nearest even) when staged, halving the staging traffic
  *                of both kernels at the cost of a second rounding per
  *                partial; the reduce still sums in float32 in fixed order.
+ *   interleave   tiles per destination visit of GEMM_RS_SWIZZLE_TILE_INTERLEAVED
+ *                (round j takes each destination's tiles [j*q, (j+1)*q));
+ *                0 or 1: one tile per visit; more than 1 with another
+ *                swizzle is INVALID_ARG.  A q of at least a chunk's tile
+ *                count gives the chunk-major remote-first order.
  */
 typedef struct gemm_rs_desc {
     int64_t M, N, K;
@@ -128,6 +134,7 @@ typedef struct gemm_rs_desc {
     int64_t ldc;
     uint32_t timeout_ms;
     uint32_t staging_dtype;
+    int32_t interleave;
 } gemm_rs_desc_t;
 
 typedef struct gemm_rs_plan_s *gemm_rs_plan_t;

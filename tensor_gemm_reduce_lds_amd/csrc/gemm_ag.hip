@@ -220,6 +220,7 @@ int gemm_ag_plan(const gemm_ag_desc_t *desc, gemm_ag_plan_t *out) {
     // each rank first multiplies its own chunk of X, then the chunks in the
     // order they are sent to it
     g.swizzle = GEMM_RS_SWIZZLE_SELF_FIRST;
+    g.interleave = 1;
     g.bm_shift = 0;
     while ((1 << g.bm_shift) < bm) ++g.bm_shift;
 

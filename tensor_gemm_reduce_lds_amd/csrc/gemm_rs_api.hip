@@ -87,6 +87,8 @@ int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
         d.swizzle != GEMM_RS_SWIZZLE_IDENTITY &&
         d.swizzle != GEMM_RS_SWIZZLE_TILE_INTERLEAVED)
         return GEMM_RS_ERR_INVALID_ARG;
+    if (d.interleave < 0 || (d.interleave > 1 && d.swizzle != GEMM_RS_SWIZZLE_TILE_INTERLEAVED))
+        return GEMM_RS_ERR_INVALID_ARG;
     if ((d.has_c != 0 && d.has_c != 1) || d.ldc < 0 ||
         (d.has_c && d.ldc != 0 && d.ldc < d.N))
         return GEMM_RS_ERR_INVALID_ARG;
@@ -201,6 +203,8 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     // more tile-rows per group than the matrix has changes nothing
     g.group_m = d.group_m < g.tiles_m ? d.group_m : g.tiles_m;
     g.swizzle = d.swizzle;
+    // more tiles per visit than the largest chunk holds changes nothing
+    g.interleave = d.interleave > 1 ? (d.interleave < g.T ? d.interleave : g.T) : 1;
     g.bm_shift = 0;
     while ((1 << g.bm_shift) < bm) ++g.bm_shift;
     p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;

@@ -19,6 +19,7 @@ constexpr int kThreads = 256;
 struct TileGeom {
     int64_t M, N, K, Mc;
     int32_t W, BM, BN, tiles_m, tiles_n, T, group_m, swizzle;
+    int32_t interleave;  // q >= 1: tiles per destination visit (tile-interleaved order)
     int32_t bm_shift;    // log2(BM)
 };
 
@@ -64,8 +65,9 @@ __host__ __device__ inline int32_t tile_in_chunk(const TileGeom &g, int32_t d, u
 // Tile of workgroup b: rank r = b % W takes its k-th tile, k = b / W.
 // Chunk-major orders: rank r walks destination chunks dest(r, 0..W-1), each
 // chunk's tiles in their within-chunk order.  Tile-interleaved order: rank
-// r visits dest(r, 0..W-1) in turn and takes the next tile of each on every
-// visit (visit j takes a chunk's j-th tile), skipping used-up chunks.
+// r visits dest(r, 0..W-1) in turn and takes the next q tiles of each on
+// every visit (round j takes a chunk's tiles [j*q, (j+1)*q)), skipping
+// used-up chunks.
 __host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
                                               int32_t *rank, int32_t *tile) {
     const uint32_t W = (uint32_t)g.W;
@@ -73,43 +75,52 @@ __host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
     uint32_t k = b / W;
     *rank = (int32_t)r;
     if (g.swizzle == GEMM_RS_SWIZZLE_TILE_INTERLEAVED) {
+        // round j takes each destination's tiles [j*q, (j+1)*q), fewer
+        // where a chunk runs out, in the visit order dest(r, 0..W-1)
+        const uint32_t q = (uint32_t)g.interleave;
         uint32_t n_min = 0xffffffffu, n_max = 0;
         for (int32_t d = 0; d < g.W; ++d) {
             const uint32_t n = chunk_tiles(g, d);
             n_min = n < n_min ? n : n_min;
             n_max = n > n_max ? n : n_max;
         }
-        uint32_t j, s;
-        if (k < W * n_min) {           // every chunk still has tiles
-            j = k / W;
-            s = k - j * W;
-        } else {
-            // visits before round j: cb(j) = sum_d min(n_d, j); find the
-            // last round j with cb(j) <= k (cb(n_max) = T > k)
-            auto cb = [&](uint32_t jj) {
-                uint32_t c = 0;
-                for (int32_t d = 0; d < g.W; ++d) {
-                    const uint32_t n = chunk_tiles(g, d);
-                    c += n < jj ? n : jj;
-                }
-                return c;
-            };
-            uint32_t lo = n_min, hi = n_max - 1;
-            while (lo < hi) {
-                const uint32_t mid = lo + (hi - lo + 1) / 2;
-                if (cb(mid) <= k) lo = mid;
-                else hi = mid - 1;
-            }
-            j = lo;
-            uint32_t q = k - cb(j);    // the q-th chunk (in visit order) still open
-            for (s = 0; s < W; ++s) {
-                if (chunk_tiles(g, dest_chunk(g, (int32_t)r, (int32_t)s)) > j) {
-                    if (q == 0) break;
-                    --q;
-                }
-            }
+        const uint32_t full = n_min / q;   // rounds in which every chunk gives q tiles
+        if (k < W * q * full) {
+            const uint32_t j = k / (W * q), rem = k - j * (W * q);
+            const uint32_t s = rem / q;
+            *tile = tile_in_chunk(g, dest_chunk(g, (int32_t)r, (int32_t)s), j * q + (rem - s * q));
+            return;
         }
-        *tile = tile_in_chunk(g, dest_chunk(g, (int32_t)r, (int32_t)s), j);
+        // tiles taken before round j: cb(j) = sum_d min(n_d, j*q); find the
+        // last round j with cb(j) <= k (cb(full) <= k < cb(ceil(n_max/q)) = T)
+        auto cb = [&](uint32_t jj) {
+            uint32_t c = 0;
+            for (int32_t d = 0; d < g.W; ++d) {
+                const uint32_t n = chunk_tiles(g, d);
+                c += n < jj * q ? n : jj * q;
+            }
+            return c;
+        };
+        uint32_t lo = full, hi = (n_max + q - 1) / q - 1;
+        while (lo < hi) {
+            const uint32_t mid = lo + (hi - lo + 1) / 2;
+            if (cb(mid) <= k) lo = mid;
+            else hi = mid - 1;
+        }
+        const uint32_t j = lo;
+        uint32_t rem = k - cb(j);
+        for (uint32_t s = 0; s < W; ++s) {
+            const int32_t c = dest_chunk(g, (int32_t)r, (int32_t)s);
+            const uint32_t n = chunk_tiles(g, c);
+            const uint32_t left = n > j * q ? n - j * q : 0;
+            const uint32_t avail = left < q ? left : q;
+            if (rem < avail) {
+                *tile = tile_in_chunk(g, c, j * q + rem);
+                return;
+            }
+            rem -= avail;
+        }
+        *tile = 0;   // unreachable for k < T
         return;
     }
     for (int32_t s = 0; s < g.W; ++s) {

@@ -44,7 +44,7 @@ class gemm_rs_desc_t(ctypes.Structure):
         ("groups", ctypes.c_int32), ("swizzle", ctypes.c_int32),
         ("has_c", ctypes.c_int32), ("materialize_sub", ctypes.c_int32),
         ("ldc", ctypes.c_int64), ("timeout_ms", ctypes.c_uint32),
-        ("staging_dtype", ctypes.c_uint32),
+        ("staging_dtype", ctypes.c_uint32), ("interleave", ctypes.c_int32),
     ]
 
 
@@ -159,12 +159,13 @@ def _stream_handle(stream) -> Optional[int]:
 def make_desc(M, N, K, W, dtype=BF16, tile_m=0, tile_n=0, group_m=0,
               order=ORDER_FLAT, groups=1, swizzle=SWIZZLE_REMOTE_FIRST,
               has_c=0, ldc=0, materialize_sub=0, timeout_ms=0,
-              staging_dtype=0) -> gemm_rs_desc_t:
+              staging_dtype=0, interleave=0) -> gemm_rs_desc_t:
     return gemm_rs_desc_t(M=M, N=N, K=K, W=W, dtype=dtype, tile_m=tile_m,
                           tile_n=tile_n, group_m=group_m, order=order,
                           groups=groups, swizzle=swizzle, has_c=int(has_c),
                           materialize_sub=int(materialize_sub), ldc=ldc,
-                          timeout_ms=timeout_ms, staging_dtype=staging_dtype)
+                          timeout_ms=timeout_ms, staging_dtype=staging_dtype,
+                          interleave=interleave)
 
 
 # ---- the C entry points, same names --------------------------------------

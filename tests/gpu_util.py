@@ -97,7 +97,7 @@ def geometry(w: I.Workload, plan: G.Plan) -> O.Geometry:
     d = plan.desc
     return O.Geometry(w.M, w.N, w.K, w.W, plan.info.tile_m, plan.info.tile_n,
                       group_m=plan.info.group_m, swizzle=d.swizzle,
-                      order=d.order, groups=d.groups)
+                      order=d.order, groups=d.groups, interleave=d.interleave)
 
 
 def sync():

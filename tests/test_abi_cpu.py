@@ -79,6 +79,7 @@ BAD = [
     dict(M=2**31, W=1), dict(K=2**31 + 64),
     dict(staging_dtype=2), dict(staging_dtype=1, dtype=1, tile_m=64, tile_n=64),
     dict(staging_dtype=1, materialize_sub=1, order=1, groups=2),
+    dict(interleave=-1, swizzle=3), dict(interleave=2),
 ]
 
 

@@ -74,6 +74,7 @@ def test_materialised_two_level_matches_register_two_level():
                                   dict(swizzle=G.SWIZZLE_IDENTITY),
                                   dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED),
                                   dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, group_m=3),
+                                  dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=3),
                                   dict(group_m=2), dict(group_m=3)])
 def test_tile_order_does_not_change_bits(over):
     w = dict(SMALL)["bf16_256x256_ragged"]
@@ -94,6 +95,14 @@ ORDER_CASES = [
     ("ragged_2lvl", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, group_m=3)),
     ("decode", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED)),
     ("tiny_f32", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED)),
+    # q tiles per destination visit: equal chunks (closed form), ragged
+    # chunks (binary-searched tail), and q beyond a chunk's tile count
+    ("llama70b", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=16)),
+    ("llama70b", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=32)),
+    ("ragged_2lvl", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, group_m=3, interleave=5)),
+    ("ragged_2lvl", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=100)),
+    ("decode", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=3)),
+    ("tiny_f32", dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED, interleave=3)),
 ]
 
 
@@ -264,10 +273,11 @@ def test_edge_full_parity(name, w, over):
 
 def test_edge_tile_orders_bit_exact():
     for name, w, over in EDGE:
-        for swz in (G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_TILE_INTERLEAVED):
-            with G.Plan(**desc_fields(w, **dict(over, swizzle=swz))) as plan:
+        for swz, q in ((G.SWIZZLE_REMOTE_FIRST, 0), (G.SWIZZLE_TILE_INTERLEAVED, 0),
+                       (G.SWIZZLE_TILE_INTERLEAVED, 3)):
+            with G.Plan(**desc_fields(w, **dict(over, swizzle=swz, interleave=q))) as plan:
                 assert np.array_equal(plan.tile_order(), geometry(w, plan).trace()), \
-                    (name, swz)
+                    (name, swz, q)
 
 
 @pytest.mark.parametrize("dtype,ldc", [("bf16", 0), ("bf16", 256), ("f32", 0)])
