@@ -462,6 +462,17 @@ def main():
     red_gbps = red_bytes / (red_ms * 1e-3) / 1e9
     traffic = stored_traffic() if w.name == "llama70b" else None
     info = plan.info
+    # the GEMM kernel's bound: MFMA above the ridge point (peak flop/s over
+    # peak bytes/s), HBM below it (the m <= 64 decode shard)
+    if flops / gemm_bytes >= peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
+                    "traffic": traffic}
+    else:
+        gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic}
 
     result = {
         "metric": METRIC,
@@ -481,10 +492,7 @@ def main():
                    "bias": ("row-broadcast" if w.ldc == 0 else "full") if w.has_c else None,
                    "tile": "%dx%d" % (info.tile_m, info.tile_n), "order": w.order,
                    "staging": "fp32", "parallelism": "1 GPU, %d virtual ranks" % w.W},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / peak, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
         "gemm_kernel_ms": round(gemm_ms, 4),
         "gemm_kernel_ms_median": round(gemm_list[len(gemm_list) // 2], 4),
         "gemm_kernel_ms_min": round(gemm_list[0], 4),
