@@ -87,7 +87,8 @@ typedef struct gemm_ag_info {
  * gemm_ag_plan: validate, allocate the gathered buffers, signals, error
  * word and the second stream, zero the signals (synchronously).
  * Returns OK, INVALID_ARG (NULL pointers, W, M % W, pad != 0, ...),
- * UNSUPPORTED (tile, N % tile_n, K % 64, sizes) or HIP.
+ * UNSUPPORTED (tile, N % tile_n, K % 64, sizes: each below 2^31, K below
+ * 2^23 and N below 2^25) or HIP.
  */
 GEMM_RS_API int gemm_ag_plan(const gemm_ag_desc_t *desc, gemm_ag_plan_t *out_plan);
 

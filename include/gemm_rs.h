@@ -172,7 +172,9 @@ typedef struct gemm_rs_info {
  * K < 0, M % W != 0,
  * unknown enum, bad ldc, materialize_sub without the two-level order),
  * UNSUPPORTED (tile not in the set above, N % tile_n != 0, K % 64 != 0,
- * ldc % 8 != 0, M, N or K of 2^31 or more, grid over 2^31-1) or HIP.  Invalid descriptors are
+ * ldc % 8 != 0, M, N or K of 2^31 or more, bf16 with K of 2^23 or more or
+ * N of 2^25 or more (32-bit offsets in one K step's operand windows), grid
+ * over 2^31-1) or HIP.  Invalid descriptors are
  * rejected before any HIP call.  On failure *out is set to NULL.
  */
 GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);

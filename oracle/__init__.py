@@ -65,6 +65,7 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     shape not in ``supported_tiles``, N not a multiple of the tile width,
     K not a multiple of the 64-deep K step, a C row pitch that is not a
     multiple of 8 elements (16-byte rows), M, N or K of 2^31 or more,
+    bfloat16 with K of 2^23 or more or N of 2^25 or more,
     a grid too large for 32-bit workgroup ids, or bfloat16 staging with
     float32 inputs or with the materialised two-level buffers.
     """
@@ -109,6 +110,9 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
     if staging_dtype == STAGING_BF16 and (dtype != BF16 or materialize_sub):
         return UNSUPPORTED
     if max(M, N, K) > 2**31 - 1:
+        return UNSUPPORTED
+    # bf16 kernel limit: 32-bit offsets inside one K step's operand windows
+    if dtype == BF16 and (K >= 2**23 or N >= 2**25):
         return UNSUPPORTED
     tiles = -(-M // tile_m) * (N // tile_n)
     if tiles * W > 2**31 - 1:
@@ -474,6 +478,8 @@ def validate_ag(M, N, K, W, tile_m, tile_n, group_m=0, pad=0,
     if tile_m == 0 or tile_n == 0 or N % tile_n != 0 or K % K_STEP != 0:
         return UNSUPPORTED
     if max(M, N, K) > 2**31 - 1:
+        return UNSUPPORTED
+    if K >= 2**23 or N >= 2**25:
         return UNSUPPORTED
     if -(-M // tile_m) * (N // tile_n) * W > 2**31 - 1:
         return UNSUPPORTED

@@ -173,6 +173,8 @@ int validate_ag(const gemm_ag_desc_t &d, int32_t bm, int32_t bn) {
     if (!bf16_tile_supported(bm, bn)) return GEMM_RS_ERR_UNSUPPORTED;
     if (d.N % bn != 0 || d.K % kKStepAg != 0) return GEMM_RS_ERR_UNSUPPORTED;
     if (d.M > INT32_MAX || d.N > INT32_MAX || d.K > INT32_MAX) return GEMM_RS_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets of the GEMM's per-step operand windows
+    if (d.K >= (int64_t(1) << 23) || d.N >= (int64_t(1) << 25)) return GEMM_RS_ERR_UNSUPPORTED;
     const int64_t tiles_m = (d.M + bm - 1) / bm;
     if (tiles_m * (d.N / bn) * d.W > INT32_MAX) return GEMM_RS_ERR_UNSUPPORTED;
     // copy items are counted in 32 bits

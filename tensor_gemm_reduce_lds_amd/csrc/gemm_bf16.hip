@@ -5,7 +5,7 @@
 //
 // Mainloop, per BK-deep K step:
 //   * A[BM][BK] and B[BK][BN] tiles go from HBM straight into LDS with
-//     16-byte global_load_lds (no register staging) into a ring of STAGES
+//     16-byte buffer loads to LDS (no register staging) into a ring of STAGES
 //     LDS stages; loads run STAGES-1 steps ahead of the MFMAs.  The DMA is
 //     issued from inline asm and its completion tracked by explicit vmcnt
 //     waits, so the compiler does not serialise LDS reads of one stage
@@ -45,11 +45,29 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
-// 16 bytes per lane from global memory straight into LDS: lane l's data
-// lands at lds_base + 16*l (lds_base is wave-uniform, passed in M0).
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_base) : "memory", "m0");
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, `bytes`
+// records, 32-bit untyped data format.  A load at an offset of `bytes` or
+// more returns zeros instead of touching memory.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    i32x4_t r;
+    r[0] = (int32_t)(uint32_t)p;
+    r[1] = (int32_t)((uint32_t)(p >> 32) & 0xffffu);
+    r[2] = (int32_t)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// the buffer at its byte offset `voff` and its data lands at
+// lds_base + 16*l (lds_base is wave-uniform, passed in M0).  The buffer
+// form takes a 32-bit offset per lane instead of a 64-bit address, half the
+// address traffic of the global form (measured +3.5% on the whole GEMM).
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_base) : "memory", "m0");
 }
 
 // A workgroup barrier for LDS hand-offs only: it waits for this wave's LDS
@@ -145,32 +163,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     const uint16_t *B = (const uint16_t *)a.B + (int64_t)r * g.K * g.N;
     const int64_t row0 = (int64_t)tm * BM, col0 = (int64_t)tn * BN;
 
-    // ---- per-lane DMA sources (k offset added per step) ----
-    const uint16_t *a_src[A_ISSUES];
+    // ---- per-lane DMA byte offsets inside one K step's windows ----
+    // Step kt reads the A window (the tile's rows, columns [kt*BK, +BK))
+    // from a descriptor based at A[row0][kt*BK] and the B window (rows
+    // [kt*BK, +BK), the tile's columns) from one based at B[kt*BK][col0];
+    // the per-lane offsets stay the same every step and fit 32 bits
+    // (K < 2^23, N < 2^25: plan limits).
+    const int64_t a_rows = g.M - row0 < BM ? g.M - row0 : BM;
+    const uint32_t a_bytes = (uint32_t)(((a_rows - 1) * g.K + BK) * 2);
+    const uint32_t b_bytes = (uint32_t)(((int64_t)(BK - 1) * g.N + BN) * 2);
+    uint32_t a_voff[A_ISSUES];
 #pragma unroll
     for (int i = 0; i < A_ISSUES; ++i) {
         const int m = (i * NW + wave) * A_ROWS + lane / CPA;
-        int64_t row = row0 + m;
-        if (row > g.M - 1) row = g.M - 1;   // ragged M: fetch a valid row
-        a_src[i] = A + row * g.K + ((lane % CPA) ^ swa<BK>(m)) * 8;
+        const int64_t ml = m < a_rows ? m : a_rows - 1;   // ragged M: fetch a valid row
+        a_voff[i] = (uint32_t)((ml * g.K + ((lane % CPA) ^ swa<BK>(m)) * 8) * 2);
     }
-    const uint16_t *b_src[B_ISSUES];
+    uint32_t b_voff[B_ISSUES];
 #pragma unroll
     for (int i = 0; i < B_ISSUES; ++i) {
         const int k = (i * NW + wave) * B_ROWS + lane / CPR;
-        b_src[i] = B + (int64_t)k * g.N + col0 + ((lane % CPR) ^ swb(k)) * 8;
+        b_voff[i] = (uint32_t)(((int64_t)k * g.N + ((lane % CPR) ^ swb(k)) * 8) * 2);
     }
 
     auto issue = [&](int kt, int buf) {
         const uint32_t As = smem_base + buf * STAGE;
         const uint32_t Bs = As + A_BYTES;
-        const int64_t ka = (int64_t)kt * BK, kb = (int64_t)kt * BK * g.N;
+        const i32x4_t a_rsrc = buffer_rsrc(A + row0 * g.K + (int64_t)kt * BK, a_bytes);
+        const i32x4_t b_rsrc = buffer_rsrc(B + (int64_t)kt * BK * g.N + col0, b_bytes);
 #pragma unroll
         for (int i = 0; i < A_ISSUES; ++i)
-            dma16(a_src[i] + ka, As + (i * NW + wave) * 1024);
+            dma16(a_rsrc, a_voff[i], As + (i * NW + wave) * 1024);
 #pragma unroll
         for (int i = 0; i < B_ISSUES; ++i)
-            dma16(b_src[i] + kb, Bs + (i * NW + wave) * 1024);
+            dma16(b_rsrc, b_voff[i], Bs + (i * NW + wave) * 1024);
     };
 
     // ---- per-lane LDS read offsets (bytes, within a stage) ----

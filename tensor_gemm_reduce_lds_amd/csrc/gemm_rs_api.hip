@@ -47,6 +47,8 @@ namespace {
 
 constexpr int kMaxW = 64;
 constexpr int kKStep = 64;
+constexpr int64_t kMaxKBf16 = int64_t(1) << 23;
+constexpr int64_t kMaxNBf16 = int64_t(1) << 25;
 
 bool f32_tile_supported(int32_t bm, int32_t bn) { return bm == 64 && bn == 64; }
 
@@ -106,6 +108,10 @@ int validate(const gemm_rs_desc_t &d, int32_t bm, int32_t bn) {
         (d.dtype != GEMM_RS_BF16 || d.materialize_sub))
         return GEMM_RS_ERR_UNSUPPORTED;
     if (d.M > INT32_MAX || d.N > INT32_MAX || d.K > INT32_MAX)
+        return GEMM_RS_ERR_UNSUPPORTED;
+    // the bf16 kernel addresses one K step's A and B windows with 32-bit
+    // buffer offsets: up to 256 rows of K and 64 rows of N elements
+    if (d.dtype == GEMM_RS_BF16 && (d.K >= kMaxKBf16 || d.N >= kMaxNBf16))
         return GEMM_RS_ERR_UNSUPPORTED;
     int64_t tiles = ((d.M + bm - 1) / bm) * (d.N / bn);
     if (tiles * d.W > INT32_MAX) return GEMM_RS_ERR_UNSUPPORTED;

@@ -80,6 +80,7 @@ BAD = [
     dict(staging_dtype=2), dict(staging_dtype=1, dtype=1, tile_m=64, tile_n=64),
     dict(staging_dtype=1, materialize_sub=1, order=1, groups=2),
     dict(interleave=-1, swizzle=3), dict(interleave=2),
+    dict(K=2**23), dict(N=2**25), dict(N=2**25 + 256),
 ]
 
 
@@ -105,7 +106,7 @@ def test_ag_null_handles_and_flags():
 
 AG_BAD = [dict(W=0), dict(W=65), dict(M=1000, W=3), dict(M=0), dict(K=0), dict(pad=1),
           dict(group_m=-1), dict(tile_m=-64), dict(tile_m=128, tile_n=64), dict(N=1000),
-          dict(K=100), dict(M=2**31, W=1),
+          dict(K=100), dict(M=2**31, W=1), dict(K=2**23), dict(N=2**25),
           # 2^23 tile-rows x 64 ranks x 16 copy pieces overflows 32 bits
           dict(M=2**29, N=128, K=64, W=64, tile_m=64, tile_n=128)]
 

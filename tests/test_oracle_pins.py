@@ -517,6 +517,10 @@ TILES = [(256, 256), (64, 64)]
     (dict(tile_m=128, tile_n=128), O.UNSUPPORTED),
     (dict(N=1000), O.UNSUPPORTED),
     (dict(K=100), O.UNSUPPORTED),
+    (dict(K=2**23 - 64), O.OK),
+    (dict(K=2**23), O.UNSUPPORTED),
+    (dict(N=2**25 - 256), O.OK),
+    (dict(N=2**25), O.UNSUPPORTED),
     (dict(swizzle=O.TILE_INTERLEAVED), O.OK),
     (dict(swizzle=O.TILE_INTERLEAVED, interleave=32), O.OK),
     (dict(interleave=1), O.OK),
@@ -633,6 +637,8 @@ def test_ag_gemm_rows_exact_integers():
     (dict(group_m=-1), O.INVALID_ARG),
     (dict(N=1000), O.UNSUPPORTED),
     (dict(K=100), O.UNSUPPORTED),
+    (dict(K=2**23), O.UNSUPPORTED),
+    (dict(N=2**25), O.UNSUPPORTED),
     (dict(tile_m=128, tile_n=64), O.UNSUPPORTED),
 ])
 def test_validate_ag_table(kw, code):
