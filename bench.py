@@ -141,7 +141,9 @@ def ablation_measure(plan, A, B, C, out, w, stream, steps):
     headline (none is a target).  kernel-sync: every step followed by a
     stream synchronisation.  clear-kernel: the staging buffer cleared before
     every step, the memset a design that accumulates in place would need
-    (this one stores per-source slots and never clears).  Cold reduce: the
+    (this one stores per-source slots and never clears).  clear-only: the
+    memset and a synchronisation alone.  clear-kernel-sync: memset, sync,
+    step, sync.  Cold reduce: the
     GEMM alone, then a 512 MiB write that flushes the memory-side cache,
     then the reduce alone.  Context: torch.bmm (hipBLASLt) on the same W
     GEMMs with a bfloat16 output and no scatter; the library never calls it."""
@@ -182,6 +184,26 @@ def ablation_measure(plan, A, B, C, out, w, stream, steps):
     clear_ms = (time.perf_counter() - t0) * 1e3 / n
     check("clear-kernel")
 
+    # clear-only (the memset and the synchronisation, no kernel) and
+    # clear-kernel-sync (memset, sync, step, sync); the pages' host barrier
+    # between ranks has no counterpart with one process
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        if hip.hipMemsetAsync(info.staging, 0, info.staging_bytes, stream.cuda_stream) != 0:
+            raise RuntimeError("hipMemsetAsync failed")
+        stream.synchronize()
+    clear_only_ms = (time.perf_counter() - t0) * 1e3 / n
+    t0 = time.perf_counter()
+    for _ in range(n):
+        if hip.hipMemsetAsync(info.staging, 0, info.staging_bytes, stream.cuda_stream) != 0:
+            raise RuntimeError("hipMemsetAsync failed")
+        stream.synchronize()
+        run()
+        stream.synchronize()
+    clear_sync_ms = (time.perf_counter() - t0) * 1e3 / n
+    check("clear-kernel-sync")
+
     flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=out.device)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cold = []
@@ -200,6 +222,8 @@ def ablation_measure(plan, A, B, C, out, w, stream, steps):
     result = {
         "kernel_sync_ms_per_step": round(sync_ms, 4),
         "clear_kernel_ms_per_step": round(clear_ms, 4),
+        "clear_only_ms": round(clear_only_ms, 4),
+        "clear_kernel_sync_ms_per_step": round(clear_sync_ms, 4),
         "clear_bytes": int(info.staging_bytes),
         "cold_reduce_ms": round(cold_ms, 4),
         "cold_reduce_gbps": round(red_bytes / (cold_ms * 1e-3) / 1e9, 1),
