@@ -77,6 +77,20 @@ def algorithmic_bytes(w, elem):
     return gemm, red
 
 
+def gemm_roofline(flops, gemm_bytes, gemm_ms, peak_tflops, traffic):
+    """The GEMM kernel's roofline object: MFMA-bound above the ridge point
+    (peak flop/s over peak bytes/s), HBM-bound below it (the m <= 64 decode
+    shard), with the achieved rate from algorithmic flops or bytes."""
+    if flops / gemm_bytes >= peak_tflops * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        tflops = flops / (gemm_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tflops,
+                "unit": "TFLOP/s", "frac": round(tflops / peak_tflops, 4),
+                "traffic": traffic}
+    gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": traffic}
+
+
 def cpu_baseline(w, x, budget_s: float):
     """Time the oracle (fp64 reference rows, every rank, OpenMP over rows)
     on the first rows of the workload for about budget_s seconds."""
@@ -486,17 +500,7 @@ def main():
     red_gbps = red_bytes / (red_ms * 1e-3) / 1e9
     traffic = stored_traffic() if w.name == "llama70b" else None
     info = plan.info
-    # the GEMM kernel's bound: MFMA above the ridge point (peak flop/s over
-    # peak bytes/s), HBM below it (the m <= 64 decode shard)
-    if flops / gemm_bytes >= peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
-        roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                    "traffic": traffic}
-    else:
-        gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": traffic}
+    roofline = gemm_roofline(flops, gemm_bytes, gemm_ms, peak, traffic)
 
     result = {
         "metric": METRIC,
