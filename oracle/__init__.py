@@ -179,7 +179,10 @@ class Geometry:
         return ((d * self.W + r) * self.Mc + (i - d * self.Mc)) * self.N + j
 
     def sub_offset(self, d: int, g: int, i: int, j: int) -> int:
-        """Offset in the materialised two-level buffer sub[d][G][Mc][N]."""
+        """Element offset of (row i, col j) of group g's partial sum in the
+        materialised two-level buffer sub[d][G][Mc][N]: for destination d,
+        one Mc x N block per group of ranks (the sub-node partial buffer of
+        page "flux实现：sm80 gemm+rs", section "2D Ring优化")."""
         return ((d * self.groups + g) * self.Mc + (i - d * self.Mc)) * self.N + j
 
     # -- swizzle ----------------------------------------------------------
@@ -432,17 +435,30 @@ def bf16_bits_to_f64(h) -> np.ndarray:
 # --------------------------------------------------------------------------
 # error measures (the parity bar)
 # --------------------------------------------------------------------------
-def rel_frobenius(got, ref) -> float:
+def _same_shape(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref)
-    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+    # no broadcasting: a result of the wrong shape is a failure, not a
+    # smaller comparison
+    if got.shape != ref.shape:
+        raise ValueError("shape mismatch: got %s, ref %s" % (got.shape, ref.shape))
+    return got, ref
+
+
+def rel_frobenius(got, ref) -> float:
+    """||got - ref||_F / ||ref||_F over all elements (the aggregate half of
+    the accuracy bar).  A zero reference has no scale: the error is then
+    ||got||_F itself (0 only for an all-zero result)."""
+    got, ref = _same_shape(got, ref)
+    den = np.sqrt(np.sum(ref * ref))
+    num = np.sqrt(np.sum((got - ref) * (got - ref)))
+    return float(num / (den if den > 0 else 1.0))
 
 
 def max_norm_err(got, ref) -> float:
-    """max |got - ref| / max(1, |ref|) over all elements."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    """max |got - ref| / max(1, |ref|) over all elements (the elementwise
+    half of the accuracy bar: absolute below |ref| = 1, relative above)."""
+    got, ref = _same_shape(got, ref)
     if got.size == 0:
         return 0.0
     return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))

@@ -20,19 +20,14 @@ namespace {
 constexpr int kCopyThreads = 256;
 // each tile-row of X is copied as kSubBlocks pieces (a power of two, so the
 // per-tile-row arrival counters stay consistent across 32-bit wrap-around)
-#ifndef GEMM_AG_SUB_BLOCKS
-#define GEMM_AG_SUB_BLOCKS 16
-#endif
-constexpr uint32_t kSubBlocks = GEMM_AG_SUB_BLOCKS;
+constexpr uint32_t kSubBlocks = 16;
 static_assert((kSubBlocks & (kSubBlocks - 1)) == 0, "power of two");
 // The copies must run beside a GEMM whose resident tiles wait for them: a
 // copy wave's registers have to fit in what every GEMM tile configuration
 // leaves free on a SIMD at its own maximum occupancy (the test suite checks
 // this against the compiler's resource report; the copy loop is kept
 // shallow for it).  Workgroups of the persistent copy grid: one per CU.
-#ifndef GEMM_AG_COPY_GRID
-#define GEMM_AG_COPY_GRID 256
-#endif
+constexpr uint32_t kCopyGrid = 256;
 
 struct AgCopyArgs {
     TileGeom g;
@@ -121,7 +116,7 @@ __global__ __launch_bounds__(kCopyThreads) void ag_copy_kernel(AgCopyArgs a) {
 
 hipError_t launch_ag_copy(const AgCopyArgs &a, hipStream_t s) {
     const uint32_t items = (uint32_t)a.g.W * (uint32_t)a.g.tiles_m * kSubBlocks;
-    const uint32_t grid = items < GEMM_AG_COPY_GRID ? items : GEMM_AG_COPY_GRID;
+    const uint32_t grid = items < kCopyGrid ? items : kCopyGrid;
     hipLaunchKernelGGL(ag_copy_kernel, dim3(grid), dim3(kCopyThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -242,11 +237,13 @@ int gemm_ag_plan(const gemm_ag_desc_t *desc, gemm_ag_plan_t *out) {
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ready, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->copied, hipEventDisableTiming);
-    // signals are zeroed once; every later run publishes a new epoch
-    if (e == hipSuccess) e = hipMemset(p->signals, 0, p->signals_bytes);
-    if (e == hipSuccess) e = hipMemset(p->arrived, 0, p->signals_bytes);
-    if (e == hipSuccess) e = hipMemset(p->err, 0, 16);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
+    // signals are zeroed once; every later run publishes a new epoch.  The
+    // zeroing runs on the plan's own stream and only that stream is waited
+    // for (unrelated work on the device is not)
+    if (e == hipSuccess) e = hipMemsetAsync(p->signals, 0, p->signals_bytes, p->copy);
+    if (e == hipSuccess) e = hipMemsetAsync(p->arrived, 0, p->signals_bytes, p->copy);
+    if (e == hipSuccess) e = hipMemsetAsync(p->err, 0, 16, p->copy);
+    if (e == hipSuccess) e = hipStreamSynchronize(p->copy);
     if (e != hipSuccess) {
         free_ag(p);
         return GEMM_RS_ERR_HIP;

@@ -541,11 +541,8 @@ bool bf16_tile_supported(int32_t bm, int32_t bn) {
 
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int bm = a.g.BM, bn = a.g.BN;
-#ifndef GEMM_RS_BK
-#define GEMM_RS_BK 64
-#define GEMM_RS_STAGES 2
-#endif
-    constexpr int BKc = GEMM_RS_BK, ST = GEMM_RS_STAGES;
+    // 64-deep K steps in two LDS stages of (BM + BN) x 64 bf16
+    constexpr int BKc = 64, ST = 2;
     if (bm == 256 && bn == 256) return launch_tile<256, 256, BKc, ST, 2, 4>(a, s);
     if (bm == 256 && bn == 128) return launch_tile<256, 128, BKc, ST, 2, 2>(a, s);
     if (bm == 128 && bn == 128) return launch_tile<128, 128, BKc, ST, 2, 2>(a, s);

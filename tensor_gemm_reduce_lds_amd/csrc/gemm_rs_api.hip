@@ -13,10 +13,7 @@ using namespace gemm_rs;
 
 // overlapped reduce: slices of the last tile-order step (remote-first
 // order), and at most this many chunk groups (identity order)
-#ifndef GEMM_RS_SLICES
-#define GEMM_RS_SLICES 4
-#endif
-constexpr int kSlices = GEMM_RS_SLICES;
+constexpr int kSlices = 4;
 constexpr int kChunkSlices = 8;
 constexpr int kEvents = kSlices > kChunkSlices ? kSlices : kChunkSlices;
 
@@ -251,10 +248,12 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
             if (chunk_first_tile_row(g, dd + 1) - chunk_first_tile_row(g, dd) != n0)
                 p->uniform_chunks = false;
     }
-    // flags are zeroed once, here; runs keep them at 0 between passes
-    if (e == hipSuccess) e = clear_protocol_state(p, nullptr);
-    if (e == hipSuccess) e = hipMemset(p->trace, 0xff, p->trace_bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
+    // flags are zeroed once, here; runs keep them at 0 between passes.  The
+    // zeroing runs on the plan's own stream and only that stream is waited
+    // for (unrelated work on the device is not)
+    if (e == hipSuccess) e = clear_protocol_state(p, p->aux);
+    if (e == hipSuccess) e = hipMemsetAsync(p->trace, 0xff, p->trace_bytes, p->aux);
+    if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
     if (e != hipSuccess) {
         free_plan(p);
         return GEMM_RS_ERR_HIP;

@@ -9,10 +9,7 @@
 namespace gemm_rs {
 
 // Reduce work unit: kReduceRows output rows of one tile.
-#ifndef GEMM_RS_REDUCE_ROWS
-#define GEMM_RS_REDUCE_ROWS 32
-#endif
-constexpr int kReduceRows = GEMM_RS_REDUCE_ROWS;
+constexpr int kReduceRows = 32;
 constexpr int kThreads = 256;
 
 // Geometry the kernels need to place tiles.

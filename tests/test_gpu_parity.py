@@ -70,6 +70,41 @@ def test_materialised_two_level_matches_register_two_level():
     assert np.array_equal(bits_reg, bits_mat)
 
 
+@pytest.mark.parametrize("groups", [2, 4])
+def test_materialised_sub_buffer_layout(groups):
+    """The materialised two-level mode writes each group's partial sum to
+    sub[d][g][Mc][N].  With entries in {-1,0,1} every partial and every
+    group sum is exact in float, so the buffer must hold, at the oracle's
+    sub_offset(d, g, i, j), the sum of the oracle's partials of the ranks in
+    group g, element for element (straddling tiles, ragged last tile-row)."""
+    w = I.with_shape(W70["ragged_2lvl"], M=560, N=512, K=128, groups=groups,
+                     tile_m=256, tile_n=256)
+    x = I.make_inputs(w, dist="ternary", c_dist="ternary")
+    dev = to_device(x, w)
+    say("sub buffer layout", groups)
+    kw = oracle_kw(w)
+    with G.Plan(**desc_fields(w, materialize_sub=1)) as plan:
+        out = new_out(w)
+        run_checked(plan, dev, w, out)
+        geom = geometry(w, plan)
+        sub = d2h(plan.info.sub, plan.info.sub_bytes, np.float32)
+        assert plan.info.sub_bytes == groups * w.M * w.N * 4
+        bits = out_bits(out)
+    parts = [O.partial_rows(x["A"], x["B"], x["C"], dtype=kw["dtype"], alpha=w.alpha,
+                            beta=w.beta, ldc=w.ldc, r=r) for r in range(w.W)]
+    L = w.W // groups
+    jj = np.arange(w.N)
+    for g in range(groups):
+        want = sum(parts[r] for r in range(g * L, (g + 1) * L))
+        for i in range(w.M):
+            off = geom.sub_offset(geom.chunk_of_row(i), g, i, 0)
+            assert off == geom.sub_offset(geom.chunk_of_row(i), g, i, jj[-1]) - (w.N - 1)
+            got = sub[off:off + w.N].astype(np.float64)
+            assert np.array_equal(got, want[i]), (g, i)
+    em = O.emulate_rows(x["A"], x["B"], x["C"], **kw)
+    assert np.array_equal(bits, em.view(bits.dtype))
+
+
 @pytest.mark.parametrize("over", [dict(swizzle=G.SWIZZLE_SELF_FIRST),
                                   dict(swizzle=G.SWIZZLE_IDENTITY),
                                   dict(swizzle=G.SWIZZLE_TILE_INTERLEAVED),

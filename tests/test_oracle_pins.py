@@ -479,6 +479,30 @@ def test_staging_offset_hand_values():
     assert G.staging_offset(1, 1, 3, 2) == 4 * 2 * 3 - 1
 
 
+def test_sub_offsets_are_a_bijection():
+    # sub[d][G][Mc][N]: every (destination, group, chunk row, column) has
+    # its own element, and together they fill G*M*N elements exactly once
+    for (M, N, W, G) in [(8, 3, 4, 2), (12, 5, 4, 4), (16, 2, 8, 2), (6, 4, 2, 1)]:
+        geo = O.Geometry(M, N, 64, W, 64, N, order=O.TWO_LEVEL, groups=G)
+        seen = np.zeros(G * M * N, dtype=np.int32)
+        for i in range(M):
+            d = geo.chunk_of_row(i)
+            for g in range(G):
+                for j in range(N):
+                    seen[geo.sub_offset(d, g, i, j)] += 1
+        assert np.all(seen == 1), (M, N, W, G)
+
+
+def test_sub_offset_hand_values():
+    # W=4, G=2, M=8 (Mc=2), N=3: block (d, g) starts at (d*2 + g)*Mc*N
+    geo = O.Geometry(8, 3, 64, 4, 64, 3, order=O.TWO_LEVEL, groups=2)
+    assert geo.sub_offset(0, 0, 0, 0) == 0
+    assert geo.sub_offset(0, 1, 0, 0) == 6          # second group of chunk 0
+    assert geo.sub_offset(1, 0, 2, 0) == 12         # chunk 1 starts after 2 groups
+    assert geo.sub_offset(1, 1, 3, 2) == 23         # ((1*2+1)*2 + 1)*3 + 2
+    assert geo.sub_offset(3, 1, 7, 2) == 2 * 8 * 3 - 1
+
+
 def test_flag_prediction():
     G = O.Geometry(128, 256, 512, 2, 64, 64)
     assert not G.predict_flags([3]).any()
@@ -645,3 +669,81 @@ def test_validate_ag_table(kw, code):
     base = dict(M=2048, N=1024, K=512, W=8, tile_m=256, tile_n=256)
     base.update(kw)
     assert O.validate_ag(**base, supported_tiles=[(256, 256), (256, 128)]) == code
+
+
+# ------------------------------------------------------- the parity measures
+def test_error_measures_hand_values():
+    # got = [1, 2], ref = [1, 3]: difference [0, -1]
+    got, ref = np.array([1.0, 2.0]), np.array([1.0, 3.0])
+    assert O.rel_frobenius(got, ref) == pytest.approx(1 / np.sqrt(10), rel=1e-15)
+    assert O.max_norm_err(got, ref) == pytest.approx(1 / 3, rel=1e-15)
+    # 2-D input: all elements count, not a row or column
+    g2 = np.array([[1.0, 2.0], [3.0, 4.0]])
+    r2 = np.array([[1.0, 2.0], [3.0, 6.0]])
+    assert O.rel_frobenius(g2, r2) == pytest.approx(2 / np.sqrt(50), rel=1e-15)
+    assert O.max_norm_err(g2, r2) == pytest.approx(2 / 6, rel=1e-15)
+    # identical inputs
+    assert O.rel_frobenius(r2, r2) == 0.0 and O.max_norm_err(r2, r2) == 0.0
+
+
+def test_max_norm_err_floor_below_one():
+    # |ref| < 1: the error is absolute (divided by 1, not by |ref|)
+    assert O.max_norm_err(np.array([0.5]), np.array([0.25])) == pytest.approx(0.25)
+    assert O.max_norm_err(np.array([1e-3]), np.array([0.0])) == pytest.approx(1e-3)
+    # |ref| > 1: relative
+    assert O.max_norm_err(np.array([9.0]), np.array([8.0])) == pytest.approx(1 / 8)
+    assert O.max_norm_err(np.array([-9.0]), np.array([-8.0])) == pytest.approx(1 / 8)
+    # the maximum over elements, mixing both regimes
+    got = np.array([0.5, 9.0, 100.5])
+    ref = np.array([0.25, 8.0, 100.0])
+    assert O.max_norm_err(got, ref) == pytest.approx(0.25)
+    assert O.max_norm_err(np.zeros(0), np.zeros(0)) == 0.0
+
+
+def test_rel_frobenius_zero_reference():
+    # no scale to divide by: the error is the result's own norm
+    assert O.rel_frobenius(np.zeros(4), np.zeros(4)) == 0.0
+    assert O.rel_frobenius(np.array([3.0, 4.0]), np.zeros(2)) == pytest.approx(5.0)
+
+
+@pytest.mark.parametrize("fn", [O.rel_frobenius, O.max_norm_err])
+def test_error_measures_reject_shape_mismatch(fn):
+    # broadcasting a [N] reference against an [M, N] result would compare
+    # less than the whole output: a mismatch must raise
+    with pytest.raises(ValueError):
+        fn(np.zeros((4, 3)), np.zeros(3))
+    with pytest.raises(ValueError):
+        fn(np.zeros((3, 4)), np.zeros((4, 3)))
+    with pytest.raises(ValueError):
+        fn(np.zeros(5), np.zeros(4))
+
+
+def test_bf16_output_floor_hand_case():
+    # 1 + 2^-9 is a quarter ulp above 1.0 in bfloat16 (ulp 2^-7): it rounds
+    # to 1.0, an error of 2^-9; 3.0 is exact
+    ref = np.array([1.0 + 2.0**-9, 3.0])
+    got = O.bf16_bits_to_f64(O.bf16_rne(ref.astype(np.float32)))
+    assert got.tolist() == [1.0, 3.0]
+    want = 2.0**-9 / np.sqrt((1 + 2.0**-9) ** 2 + 9.0)
+    assert O.rel_frobenius(got, ref) == pytest.approx(want, rel=1e-12)
+    assert O.max_norm_err(got, ref) == pytest.approx(2.0**-9 / (1 + 2.0**-9), rel=1e-12)
+
+
+def test_bf16_output_floor_on_gaussian_outputs():
+    """The accuracy floor of any bfloat16 output: rel_F(bf16_RNE(ref), ref)
+    on N(0, 8) data (W = 8 partials of unit variance).  Rounding to nearest
+    with 8 significant bits errs by at most 2^-8 of |x| (a strict bound),
+    and with the error spread evenly over +-half an ulp of the binade
+    [2^e, 2^(e+1)) its mean square is 2^(2e-16)/3, so rel_F lies between
+    2^-8/(2*sqrt(3)) (all mantissas near 2) and 2^-8/sqrt(3) (all near 1).
+    Truncation instead of rounding would double it; a dropped square root
+    would put it near 3e-6.  The floor sits below the 2e-3 bar, which is
+    why the staged partials are kept in float32."""
+    rng = np.random.default_rng(8)
+    ref = (rng.standard_normal(1 << 20) * np.sqrt(8.0)).astype(np.float32).astype(np.float64)
+    got = O.bf16_bits_to_f64(O.bf16_rne(ref.astype(np.float32)))
+    floor = O.rel_frobenius(got, ref)
+    assert floor <= 2.0**-8
+    assert 2.0**-8 / (2 * np.sqrt(3)) <= floor <= 2.0**-8 / np.sqrt(3)
+    assert floor < 2e-3
+    assert O.max_norm_err(got, ref) <= 2.0**-8
