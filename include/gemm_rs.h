@@ -80,8 +80,9 @@ extern "C" {
 #define GEMM_RS_RUN_REDUCE  2u /* flag-gated reduce (+ flag reset)          */
 #define GEMM_RS_KEEP_FLAGS  4u /* debug: the reduce leaves flags at 1       */
 #define GEMM_RS_TRACE_TILES 8u /* debug: GEMM records trace[b] = tile of WG b */
-#define GEMM_RS_OVERLAP_REDUCE 16u /* with RUN_GEMM|RUN_REDUCE: overlap the reduce
-                                      with the GEMM (see gemm_rs_run) */
+#define GEMM_RS_OVERLAP_REDUCE 16u /* with RUN_GEMM|RUN_REDUCE: take the reduce
+                                      off the serial path (owner-fused or
+                                      overlapped; see gemm_rs_run) */
 #define GEMM_RS_RUN_ALL     (GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE)
 
 /*
@@ -197,17 +198,23 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
  *   run_flags  GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE, plus the debug bits,
  *              plus GEMM_RS_OVERLAP_REDUCE
  * GEMM_RS_OVERLAP_REDUCE (both RUN bits, flat or register two-level
- * reduce, every chunk owning the same number of tile rows, remote-first or
- * identity tile order; otherwise ignored): the GEMM is launched in slices
- * of the tile order and, after each slice, an auxiliary stream owned by the
- * plan reduces exactly the tiles that slice completed, concurrently with
- * the next slice; `stream` waits for the auxiliary stream at the end.
- * Remote-first order: chunk d is complete only when rank d has computed its
- * own chunk, which that order puts in every rank's last step, so the slices
- * are the earlier steps plus four slices of the last step.  Identity order:
- * every rank computes chunk c in the same steps, so chunk c is complete
- * after them and its reduce overlaps the GEMM of the following chunks (up
- * to eight slices).  Results are bit-identical to the serial order.
+ * reduce, every chunk owning the same number of tile rows; otherwise
+ * ignored) takes the reduce off the serial path in one of two ways:
+ *   - remote-first tile order (owner-fused reduce; bf16, 256x256 tiles,
+ *     W = 8, without KEEP_FLAGS, else the serial path): every rank visits
+ *     its own chunk last, so rank d's last step is the last contribution
+ *     to every tile of chunk d, and the other ranks' partials of those
+ *     tiles come from earlier steps.  The earlier steps run as one launch;
+ *     in a second launch on `stream` each of rank d's last-step workgroups
+ *     checks and resets the other ranks' flags for its tile, sums the
+ *     tile's W partials in the reduce order (its own from registers, never
+ *     staged) and writes its rows of `out`.  No separate reduce runs.
+ *   - identity tile order: every rank computes chunk c in the same steps;
+ *     the GEMM is launched chunk group by chunk group (up to eight) and,
+ *     after each, an auxiliary stream owned by the plan reduces the chunks
+ *     it completed, concurrently with the next group; `stream` waits for
+ *     the auxiliary stream at the end.
+ * Results are bit-identical to the serial order.
  * The caller owns A, B, C, out and the stream, and keeps them alive until
  * the stream's work is done.  Calls on one stream are ordered; one plan
  * must not run on two streams at once.  A device-side flag-wait timeout or

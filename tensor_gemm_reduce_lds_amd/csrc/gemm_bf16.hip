@@ -103,7 +103,8 @@ __device__ __forceinline__ int swa(int m) {
 // them over 16 distinct 16-byte bank slots.
 __device__ __forceinline__ int swb(int k) { return 4 * (k & 3); }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+// FW > 0: the owner-fused reduce variant for W == FW ranks (see GemmArgs).
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int NW = WGM * WGN;                 // waves
     constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile
@@ -283,6 +284,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < KT) issue(s, s);
+    if constexpr (FW > 0) {
+        // owner-fused reduce: every other rank's partial of this tile was
+        // staged by an earlier launch on the stream (so it is visible
+        // here); its flag must read 1.  Checked while the first operand
+        // loads are in flight, then every flag of the tile is put back to
+        // 0 (this rank's own never left it): this workgroup is the tile's
+        // only consumer, and the flags end the run idle as after the
+        // separate reduce.
+        int failed = 0;
+        if (tid < FW && tid != r)
+            failed = wait_flag_set(a.flags + (int64_t)tid * g.T + t, a.timeout_ticks, a.err,
+                                   tid, t, false);
+        if (__syncthreads_or(failed)) {
+            wait_vmcnt<0>();                        // no DMA into LDS after exit
+            return;
+        }
+        if (tid < FW)
+            __hip_atomic_store(a.flags + (int64_t)tid * g.T + t, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     for (int kt = 0; kt < KT; ++kt) {
         // wait until this wave's DMA for step kt has landed (later steps
         // may stay in flight); the barrier makes every wave's data visible
@@ -481,6 +502,165 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             if (i + 1 < FM) lds_barrier();          // the stripe buffer is reused
         }
     };
+    // ---- owner-fused reduce epilogue ----
+    // Rank r owns every row of this tile that lies in chunk r, and this is
+    // the tile's last contribution: the other W-1 partials of each row i
+    // are in staging slots (d(i), q).  Each row's W partials are summed in
+    // the reduce order with this rank's own value (alpha*acc, plus beta*C on
+    // rows of its own chunk, rounded as staging would hold it) at position
+    // r, then rounded to bf16 and written to `out`; the own partial is
+    // never staged.  The stripes pass through LDS as in the plain epilogue,
+    // so a lane holds 4 consecutive columns of one row, the layout of the
+    // staging slots.  Loads run one row ahead of the adds and stores.
+    auto fused_epilogue = [&](auto mode_tag, auto sb_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        constexpr bool SB = decltype(sb_tag)::value;
+        constexpr int NR = FW > 1 ? FW - 1 : 1;      // remote partials per element
+        typedef typename std::conditional<SB, u32x2_t, f32x4_t>::type raw_t;
+        const int L = FW / a.groups;                 // ranks per group
+        const int64_t slot = g.Mc * g.N;             // elements from slot (d,q) to (d,q+1)
+        const int q_lo = r;                          // remote j < r is rank j, else j+1
+        float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (MODE == 1) {
+            uint2 cb_row = *(const uint2 *)(Cp + col0 + scol);
+            asm volatile("" : "+v"(cb_row.x), "+v"(cb_row.y));
+            cf[0] = __uint_as_float(cb_row.x << 16);
+            cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
+            cf[2] = __uint_as_float(cb_row.y << 16);
+            cf[3] = __uint_as_float(cb_row.y & 0xffff0000u);
+        }
+        __syncthreads();                            // every wave is done with the stages
+        // the remote partials of one row (wave-uniform row for BN = 256)
+        auto load_row = [&](int64_t base, raw_t (&v)[NR]) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                const int64_t idx = base + (int64_t)(j < q_lo ? j : j + 1) * slot;
+                if constexpr (SB)
+                    v[j] = __builtin_nontemporal_load((const u32x2_t *)((const uint16_t *)a.staging + idx));
+                else
+                    v[j] = __builtin_nontemporal_load((const f32x4_t *)((const float *)a.staging + idx));
+            }
+        };
+        auto widen = [](raw_t x) -> f32x4_t {
+            if constexpr (SB) {
+                f32x4_t v;
+                v[0] = __uint_as_float(x[0] << 16);
+                v[1] = __uint_as_float(x[0] & 0xffff0000u);
+                v[2] = __uint_as_float(x[1] << 16);
+                v[3] = __uint_as_float(x[1] & 0xffff0000u);
+                return v;
+            } else {
+                return x;
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            lds_char *stripe = smem + wm * 32 * EP_PITCH;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4_t x;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
+                    *(__attribute__((address_space(3))) f32x4_t *)(
+                        stripe + (lane & 31) * EP_PITCH + (wn * WN + j * 32 + 8 * q + h4) * 4) = x;
+                }
+            lds_barrier();                          // the stripe is in LDS
+            const int sr0 = wave * ST_PER_WAVE * RPI + srow;
+            const int64_t rowF = row0 + (sr0 >> 5) * WM + i * 32 + (sr0 & 31);
+            // row k of this lane: rowF + k*RPI; chunk and slot-0 offset per row
+            auto row_base = [&](int k, int32_t *d_out) -> int64_t {
+                int64_t row = rowF + (int64_t)k * RPI;
+                if (row > g.M - 1) row = g.M - 1;   // ragged M: a valid row, not stored
+                const int32_t d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
+                *d_out = d;
+                return (((int64_t)d * FW) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N + col0 + scol;
+            };
+            raw_t cur[NR], nxt[NR];
+            int32_t d_cur, d_nxt = 0;
+            int64_t base_cur = row_base(0, &d_cur), base_nxt = 0;
+            load_row(base_cur, cur);
+#pragma unroll
+            for (int k = 0; k < ST_PER_WAVE; ++k) {
+                if (k + 1 < ST_PER_WAVE) {          // the next row's loads go out first
+                    base_nxt = row_base(k + 1, &d_nxt);
+                    load_row(base_nxt, nxt);
+                }
+                const int64_t row = rowF + (int64_t)k * RPI;
+                f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
+                    smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
+                if constexpr (MODE != 0) {
+                    float c4[4];
+                    if constexpr (MODE == 1) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) c4[u] = cf[u];
+                    } else {
+                        const int64_t crow = row < g.M ? row : g.M - 1;
+                        const uint2 cb = *(const uint2 *)(Cp + crow * a.ldc + col0 + scol);
+                        c4[0] = __uint_as_float(cb.x << 16);
+                        c4[1] = __uint_as_float(cb.x & 0xffff0000u);
+                        c4[2] = __uint_as_float(cb.y << 16);
+                        c4[3] = __uint_as_float(cb.y & 0xffff0000u);
+                    }
+                    if (d_cur == r)                 // C counts once: on its owner's rows
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * c4[u];
+                }
+                if constexpr (SB) {
+                    // the value a bfloat16 staging slot would hold
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        x[u] = (float)(__bf16)x[u];
+                }
+                // fixed order: y = sum over groups of (sum over ranks in the
+                // group), ascending, with this rank's value at position r
+                f32x4_t y = x, sg = x;
+#pragma unroll
+                for (int q = 0; q < FW; ++q) {
+                    // rank q < r is remote partial q, rank q > r is q - 1
+                    const f32x4_t lo = widen(cur[q < NR ? q : NR - 1]);
+                    const f32x4_t hi = widen(cur[q > 0 ? q - 1 : 0]);
+                    const f32x4_t v = q == r ? x : (q < r ? lo : hi);
+                    sg = (q % L == 0) ? v : sg + v;
+                    if (q % L == L - 1) y = (q / L == 0) ? sg : y + sg;
+                }
+                if (row < g.M) {
+                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
+                    const __bf16 h2 = (__bf16)y[2], h3 = (__bf16)y[3];
+                    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    // written through past this XCD's L2, as the reduce does
+                    __hip_atomic_store((uint64_t *)((uint16_t *)a.out + row * g.N + col0 + scol),
+                                       (uint64_t)w0 | ((uint64_t)w1 << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (k + 1 < ST_PER_WAVE) {
+#pragma unroll
+                    for (int j = 0; j < NR; ++j) cur[j] = nxt[j];
+                    d_cur = d_nxt;
+                    base_cur = base_nxt;
+                }
+            }
+            if (i + 1 < FM) lds_barrier();          // the stripe buffer is reused
+        }
+    };
+    if constexpr (FW > 0) {
+        if (a.staging_bf16) {
+            if (!a.has_c) fused_epilogue(std::integral_constant<int, 0>{}, std::true_type{});
+            else if (a.ldc == 0) fused_epilogue(std::integral_constant<int, 1>{}, std::true_type{});
+            else fused_epilogue(std::integral_constant<int, 2>{}, std::true_type{});
+        } else {
+            if (!a.has_c) fused_epilogue(std::integral_constant<int, 0>{}, std::false_type{});
+            else if (a.ldc == 0) fused_epilogue(std::integral_constant<int, 1>{}, std::false_type{});
+            else fused_epilogue(std::integral_constant<int, 2>{}, std::false_type{});
+        }
+        if (tid == 0 && a.trace) a.trace[b] = t;
+        return;
+    }
+
     if (!a.has_c) epilogue(std::integral_constant<int, 0>{});
     else if (a.ldc == 0) epilogue(std::integral_constant<int, 1>{});
     else epilogue(std::integral_constant<int, 2>{});
@@ -508,7 +688,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     if (tid == 0 && a.trace) a.trace[b] = t;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW = 0>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
     constexpr size_t lds_bytes = (size_t)STAGES * (BM + BN) * BK * 2;
     static_assert(lds_bytes <= 160 * 1024, "LDS");
@@ -522,17 +702,21 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
         return hipErrorInvalidDevice;
     std::call_once(once[dev], [dev] {
         set_rc[dev] = hipFuncSetAttribute(
-            (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>,
+            (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     });
     if (set_rc[dev] != hipSuccess) return set_rc[dev];
     const int64_t blocks = a.n_blocks;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW>),
                        dim3((unsigned)blocks), dim3(64 * WGM * WGN), lds_bytes, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool fused_reduce_supported(int32_t bm, int32_t bn, int32_t W) {
+    return bm == 256 && bn == 256 && W == 8;
+}
 
 bool bf16_tile_supported(int32_t bm, int32_t bn) {
     return (bm == 256 && bn == 256) || (bm == 256 && bn == 128) ||
@@ -543,6 +727,12 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int bm = a.g.BM, bn = a.g.BN;
     // 64-deep K steps in two LDS stages of (BM + BN) x 64 bf16
     constexpr int BKc = 64, ST = 2;
+    if (a.fuse_reduce) {
+        // the owner-fused reduce exists for W = 8 with 256 x 256 tiles
+        if (bm == 256 && bn == 256 && a.g.W == 8)
+            return launch_tile<256, 256, BKc, ST, 2, 4, 8>(a, s);
+        return hipErrorInvalidValue;
+    }
     if (bm == 256 && bn == 256) return launch_tile<256, 256, BKc, ST, 2, 4>(a, s);
     if (bm == 256 && bn == 128) return launch_tile<256, 128, BKc, ST, 2, 2>(a, s);
     if (bm == 128 && bn == 128) return launch_tile<128, 128, BKc, ST, 2, 2>(a, s);

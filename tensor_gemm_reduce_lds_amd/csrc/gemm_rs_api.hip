@@ -11,11 +11,9 @@
 
 using namespace gemm_rs;
 
-// overlapped reduce: slices of the last tile-order step (remote-first
-// order), and at most this many chunk groups (identity order)
-constexpr int kSlices = 4;
+// overlapped reduce with the identity order: at most this many chunk groups
 constexpr int kChunkSlices = 8;
-constexpr int kEvents = kSlices > kChunkSlices ? kSlices : kChunkSlices;
+constexpr int kEvents = kChunkSlices;
 
 struct gemm_rs_plan_s {
     gemm_rs_desc_t d;        // resolved (tiles, group_m, timeout filled in)
@@ -357,49 +355,60 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
     r.slice_kind = kSliceAll;
     r.k_lo = r.k_hi = 0;
 
-    const bool overlap = (run_flags & GEMM_RS_OVERLAP_REDUCE) && do_gemm && do_reduce &&
-                         !p->d.materialize_sub && p->uniform_chunks &&
-                         (p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST ||
-                          p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY);
+    const bool overlap_req = (run_flags & GEMM_RS_OVERLAP_REDUCE) && do_gemm && do_reduce &&
+                             !p->d.materialize_sub && p->uniform_chunks;
+    // remote-first order: owner-fused reduce in the last step
+    const bool fused = overlap_req && p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST &&
+                       p->d.dtype == GEMM_RS_BF16 && !(run_flags & GEMM_RS_KEEP_FLAGS) &&
+                       fused_reduce_supported(p->g.BM, p->g.BN, p->g.W);
+    // identity order: chunk-by-chunk slices reduced on the second stream
+    const bool sliced = overlap_req && p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY;
     hipError_t e = hipSuccess;
-    if (overlap) {
+    if (fused) {
+        // Every rank visits its own chunk last, so rank d's last n = T/W
+        // tiles (the tiles of chunk d) are the last contribution to each of
+        // those tiles, and every other rank's partial of them comes from an
+        // earlier step.  The earlier steps run as one launch; the last step
+        // runs as a second launch on the same stream whose workgroups each
+        // sum their tile's partials and write the output directly (no
+        // separate reduce, and the own partial is never staged).
+        const uint32_t W = (uint32_t)p->g.W, T = (uint32_t)p->g.T;
+        const uint32_t k0 = T - T / W;
+        e = gemm(0, W * k0, s);
+        if (e == hipSuccess) {
+            GemmArgs x = a;
+            x.b_offset = W * k0;
+            x.n_blocks = W * (T - k0);
+            x.fuse_reduce = 1;
+            x.groups = p->d.groups;
+            x.out = out;
+            x.err = p->err;
+            x.timeout_ticks = p->timeout_ticks;
+            e = launch_gemm_bf16(x, s);
+        }
+        return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
+    }
+    if (sliced) {
         const uint32_t W = (uint32_t)p->g.W, T = (uint32_t)p->g.T;
         const uint32_t n = T / W;   // tiles per chunk (uniform)
         // GEMM steps [q0, q1) of every rank, then the reduce of the tiles
         // they completed on the auxiliary stream, concurrent with the next
-        // GEMM slice
-        auto slice = [&](int j, uint32_t q0, uint32_t q1, int kind) {
-            hipError_t x = gemm(W * q0, W * q1, s);
-            if (x == hipSuccess) x = hipEventRecord(p->slice_done[j], s);
-            if (x == hipSuccess) x = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
-            if (x == hipSuccess) {
+        // GEMM slice.  Every rank computes chunk c in steps [c*n, (c+1)*n),
+        // so chunk c is complete after them; chunks are grouped into at
+        // most kChunkSlices slices.
+        const uint32_t parts = W < (uint32_t)kChunkSlices ? W : (uint32_t)kChunkSlices;
+        for (uint32_t j = 0; j < parts && e == hipSuccess; ++j) {
+            const uint32_t q0 = n * ((W * j) / parts), q1 = n * ((W * (j + 1)) / parts);
+            e = gemm(W * q0, W * q1, s);
+            if (e == hipSuccess) e = hipEventRecord(p->slice_done[j], s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
+            if (e == hipSuccess) {
                 ReduceArgs rs = r;
-                rs.slice_kind = kind;
+                rs.slice_kind = kSliceSteps;
                 rs.k_lo = q0;
                 rs.k_hi = q1;
-                x = launch_reduce(rs, p->d.dtype, p->aux);
+                e = launch_reduce(rs, p->d.dtype, p->aux);
             }
-            return x;
-        };
-        if (p->d.swizzle == GEMM_RS_SWIZZLE_REMOTE_FIRST) {
-            // rank d's own chunk is its last n tiles (k in [T-n, T)); chunk
-            // d is complete once rank d has produced them, every other
-            // rank's share of it coming from earlier steps: the earlier
-            // steps, then slices of the last step
-            const uint32_t k0 = T - n;
-            const uint32_t parts = n < (uint32_t)kSlices ? n : (uint32_t)kSlices;
-            e = gemm(0, W * k0, s);
-            for (uint32_t j = 0; j < parts && e == hipSuccess; ++j)
-                e = slice((int)j, k0 + (n * j) / parts, k0 + (n * (j + 1)) / parts,
-                          kSliceLastStep);
-        } else {
-            // identity order: every rank computes chunk c in steps
-            // [c*n, (c+1)*n), so chunk c is complete after them; chunks are
-            // grouped into at most kChunkSlices slices
-            const uint32_t parts = W < (uint32_t)kChunkSlices ? W : (uint32_t)kChunkSlices;
-            for (uint32_t j = 0; j < parts && e == hipSuccess; ++j)
-                e = slice((int)j, n * ((W * j) / parts), n * ((W * (j + 1)) / parts),
-                          kSliceSteps);
         }
         if (e == hipSuccess) e = hipEventRecord(p->aux_done, p->aux);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, p->aux_done, 0);

@@ -152,6 +152,40 @@ __host__ __device__ inline uint32_t logical_block(const TileGeom &g, uint32_t b_
     return b_offset + k * W + r;
 }
 
+// Record the first asynchronous error of a run: {code, rank, tile, value}.
+__device__ inline void record_error(int32_t *err, int code, int32_t r, int32_t t, uint32_t v) {
+    if (atomicCAS(&err[0], 0, code) == 0) {
+        __hip_atomic_store(&err[1], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&err[2], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&err[3], (int32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Bounded wait until *f == 1 (0 = idle, 1 = ready, anything else breaks the
+// protocol).  With `acquire` the load is an agent-scope acquire (producers
+// may still be running); without it a relaxed load (producers finished in
+// an earlier launch on the stream).  Returns 0, or the error code after
+// recording it.
+__device__ inline int wait_flag_set(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
+                                    int32_t r, int32_t t, bool acquire) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        const uint32_t v =
+            acquire ? __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                    : __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v == 1u) return 0;
+        if (v != 0u) {
+            record_error(err, GEMM_RS_ERR_PROTOCOL, r, t, v);
+            return GEMM_RS_ERR_PROTOCOL;
+        }
+        if (wall_clock64() - t0 > timeout_ticks) {
+            record_error(err, GEMM_RS_ERR_TIMEOUT, r, t, 0);
+            return GEMM_RS_ERR_TIMEOUT;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 struct GemmArgs {
     TileGeom g;
     const void *A;       // [W][M][K]
@@ -177,9 +211,17 @@ struct GemmArgs {
     uint32_t epoch;
     uint64_t timeout_ticks;
     int32_t *err;
+    // owner-fused reduce (remote-first order, the launch of every rank's
+    // own-chunk tiles): workgroup (rank r, tile t) is the last contribution
+    // to tile t; it checks and resets the other ranks' flags for t, sums
+    // the tile's W partials (the others from their staging slots, its own
+    // from registers) in the reduce order and writes `out` (bf16)
+    int32_t fuse_reduce;
+    int32_t groups;         // reduce order: G groups of W/G ranks (1: flat)
+    void *out;              // [M][N]
 };
 
-enum { kSliceAll = 0, kSliceLastStep = 1, kSliceSteps = 2 };
+enum { kSliceAll = 0, kSliceSteps = 2 };
 
 struct ReduceArgs {
     TileGeom g;
@@ -194,13 +236,11 @@ struct ReduceArgs {
     uint32_t *flags;         // [W][T]
     uint32_t *counters;      // [T] (flat) or [G][T] (sub stage)
     int32_t *err;            // {code, rank, tile, value}
-    // which tiles the grid covers (steps k of the tile order, [k_lo, k_hi)):
+    // which tiles the grid covers:
     //   kSliceAll      every tile
-    //   kSliceLastStep for every chunk d, rank d's k-th tiles that lie in
-    //                  chunk d (remote-first order: rank d's own chunk, the
-    //                  last contribution to those tiles)
-    //   kSliceSteps    the k-th tile of the common order (identity order:
-    //                  every rank computes tile seq[k] in step k)
+    //   kSliceSteps    the k-th tile of the common order for k in
+    //                  [k_lo, k_hi) (identity order: every rank computes
+    //                  tile seq[k] in step k)
     int32_t slice_kind;
     uint32_t k_lo, k_hi;
     // materialised two-level buffers (sub stage writes, final stage reads)
@@ -218,5 +258,7 @@ hipError_t launch_tile_order(const TileGeom &g, int32_t *trace, hipStream_t s);
 
 // Supported bf16 tile shapes (tile_m, tile_n).
 bool bf16_tile_supported(int32_t bm, int32_t bn);
+// Configurations that have an owner-fused reduce variant of the bf16 GEMM.
+bool fused_reduce_supported(int32_t bm, int32_t bn, int32_t W);
 
 }  // namespace gemm_rs

@@ -22,35 +22,6 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ void record_error(int32_t *err, int code, int32_t r, int32_t t, uint32_t v) {
-    if (atomicCAS(&err[0], 0, code) == 0) {
-        __hip_atomic_store(&err[1], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&err[2], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&err[3], (int32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
-// Wait until *f == 1.  Returns 0, or the error code after recording it.
-__device__ int wait_ready(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
-                          int32_t r, int32_t t, bool acquire) {
-    const uint64_t t0 = wall_clock64();
-    for (;;) {
-        const uint32_t v =
-            acquire ? __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
-                    : __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v == 1u) return 0;
-        if (v != 0u) {
-            record_error(err, GEMM_RS_ERR_PROTOCOL, r, t, v);
-            return GEMM_RS_ERR_PROTOCOL;
-        }
-        if (wall_clock64() - t0 > timeout_ticks) {
-            record_error(err, GEMM_RS_ERR_TIMEOUT, r, t, 0);
-            return GEMM_RS_ERR_TIMEOUT;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-}
-
 // Threads [0, count) each wait on one flag; true if all ready.  With
 // `acquire` (producers may still be running) the waits are agent-scope
 // acquires and every thread then takes an acquire fence, so loads issued
@@ -65,8 +36,8 @@ __device__ bool wait_flags(uint32_t *base, int64_t stride, int count,
     __syncthreads();
     const int i = threadIdx.x;
     if (i < count) {
-        if (wait_ready(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile,
-                       acquire))
+        if (wait_flag_set(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile,
+                          acquire))
             atomicOr(&failed, 1);
     }
     __syncthreads();
@@ -123,10 +94,13 @@ __device__ __forceinline__ f32x4_t load_slot(const void *S, int64_t idx) {
 }
 
 // Sum of one element group (4 columns) over the W slots in the fixed order.
-// Slot q of the element group starts at element idx + q*stride.
-template <int WT, bool SB = false>
+// Slot q of the element group starts at element idx + q*stride.  WT > 0:
+// W == WT, unrolled; LT > 0: the group length L == LT, so the group
+// boundaries fold at compile time (LT == 0: L at run time).
+template <int WT, int LT, bool SB = false>
 __device__ __forceinline__ f32x4_t ordered_sum(const void *S, int64_t idx, int64_t stride,
-                                               int W, int L) {
+                                               int W, int L_rt) {
+    const int L = LT > 0 ? LT : L_rt;
     if constexpr (WT > 0) {
         f32x4_t v[WT];
 #pragma unroll
@@ -150,10 +124,11 @@ __device__ __forceinline__ f32x4_t ordered_sum(const void *S, int64_t idx, int64
 }
 
 // Two element groups at once (all 2*W loads issued before any add).
-template <int WT, bool SB>
+template <int WT, int LT, bool SB>
 __device__ __forceinline__ void ordered_sum2(const void *S, int64_t idx, int64_t idx2,
-                                             int64_t stride, int W, int L, f32x4_t *y_out,
+                                             int64_t stride, int W, int L_rt, f32x4_t *y_out,
                                              f32x4_t *y2_out) {
+    const int L = LT > 0 ? LT : L_rt;
     if constexpr (WT > 0) {
         f32x4_t v[WT], u[WT];
 #pragma unroll
@@ -174,17 +149,15 @@ __device__ __forceinline__ void ordered_sum2(const void *S, int64_t idx, int64_t
         *y_out = y;
         *y2_out = y2;
     } else {
-        *y_out = ordered_sum<0, SB>(S, idx, stride, W, L);
-        *y2_out = ordered_sum<0, SB>(S, idx2, stride, W, L);
+        *y_out = ordered_sum<0, LT, SB>(S, idx, stride, W, L);
+        *y2_out = ordered_sum<0, LT, SB>(S, idx2, stride, W, L);
     }
 }
 
 // Tile and slab of this workgroup.  kSliceAll: unit = t*U + slab.
-// kSliceLastStep: unit = ((k - k_lo)*W + d)*U + slab names rank d's k-th
-// tile, taken only if it lies in chunk d; returns false otherwise.
 // kSliceSteps: unit = (k - k_lo)*U + slab names the k-th tile of the order
 // every rank shares (rank 0's k-th tile).
-__device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32_t *slab) {
+__device__ __forceinline__ void unit_tile(const ReduceArgs &a, int32_t *t, int32_t *slab) {
     const TileGeom &g = a.g;
     const uint32_t U = (uint32_t)a.units_per_tile, unit = blockIdx.x;
     *slab = (int32_t)(unit % U);
@@ -192,31 +165,21 @@ __device__ __forceinline__ bool unit_tile(const ReduceArgs &a, int32_t *t, int32
     int32_t r;
     if (a.slice_kind == kSliceAll) {
         *t = (int32_t)rest;
-        return true;
+        return;
     }
-    if (a.slice_kind == kSliceSteps) {
-        tile_of_block(g, (a.k_lo + rest) * W, &r, t);
-        return true;
-    }
-    const int32_t d = (int32_t)(rest % W);
-    const uint32_t k = a.k_lo + rest / W;
-    const uint32_t n_d = (uint32_t)(chunk_first_tile_row(g, d + 1) - chunk_first_tile_row(g, d)) *
-                         (uint32_t)g.tiles_n;
-    if (k + n_d < (uint32_t)g.T) return false;   // rank d's k-th tile is not in chunk d
-    tile_of_block(g, k * W + (uint32_t)d, &r, t);
-    return true;
+    tile_of_block(g, (a.k_lo + rest) * W, &r, t);
 }
 
 // One-stage reduce: flags -> out.  ROWS2: two rows per thread and
 // iteration (2*W loads in flight); without it one row (W loads, fewer
 // registers: the slices that run beside the GEMM must fit in the registers
 // its workgroups leave free).  Both sum in the same order.
-template <int WT, bool OUT_BF16, bool SB, bool ROWS2 = true>
+template <int WT, int LT, bool OUT_BF16, bool SB, bool ROWS2 = true>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const TileGeom &g = a.g;
     const int32_t U = a.units_per_tile;
     int32_t t, slab;
-    if (!unit_tile(a, &t, &slab)) return;
+    unit_tile(a, &t, &slab);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t, a.acquire)) return;
@@ -244,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         for (int64_t row = lo + threadIdx.x / C4; row < hi; row += RPP) {
             const int64_t d = row / g.Mc;
             const int64_t idx = ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
-            store_out4(a.out, row * g.N + col, ordered_sum<WT, SB>(a.staging, idx, stride, W, L),
+            store_out4(a.out, row * g.N + col, ordered_sum<WT, LT, SB>(a.staging, idx, stride, W, L),
                        OUT_BF16);
         }
         return;
@@ -258,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
             const int64_t d2 = row2 / g.Mc;
             const int64_t idx2 = ((d2 * W) * g.Mc + (row2 - d2 * g.Mc)) * g.N + col;
             f32x4_t y, y2;
-            ordered_sum2<WT, SB>(a.staging, idx, idx2, stride, W, L, &y, &y2);
+            ordered_sum2<WT, LT, SB>(a.staging, idx, idx2, stride, W, L, &y, &y2);
             store_out4(a.out, row * g.N + col, y, OUT_BF16);
             store_out4(a.out, row2 * g.N + col, y2, OUT_BF16);
         } else {
-            store_out4(a.out, row * g.N + col, ordered_sum<WT, SB>(a.staging, idx, stride, W, L),
+            store_out4(a.out, row * g.N + col, ordered_sum<WT, LT, SB>(a.staging, idx, stride, W, L),
                        OUT_BF16);
         }
     }
@@ -304,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
         const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
         const int64_t d = row / g.Mc, il = row - d * g.Mc;
         const int64_t idx = ((d * g.W + (int64_t)grp * L) * g.Mc + il) * g.N + col;
-        const f32x4_t s = ordered_sum<LT>(a.staging, idx, stride, L, L);
+        const f32x4_t s = ordered_sum<LT, LT>(a.staging, idx, stride, L, L);
         float *dst = a.sub + ((d * G + grp) * g.Mc + il) * g.N + col;
         __builtin_nontemporal_store(s, (f32x4_t *)dst);
     }
@@ -343,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a
         const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
         const int64_t d = row / g.Mc, il = row - d * g.Mc;
         const int64_t idx = ((d * G) * g.Mc + il) * g.N + col;
-        const f32x4_t y = ordered_sum<0>(a.sub, idx, stride, G, G);
+        const f32x4_t y = ordered_sum<0, 0>(a.sub, idx, stride, G, G);
         store_out4(a.out, row * g.N + col, y, OUT_BF16);
     }
 }
@@ -356,24 +319,44 @@ __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     trace[b] = t;
 }
 
+// W unrolled for 1, 2, 4 and 8 slots; the group length at compile time
+// for the flat order (L = W) and two groups (L = W/2).
+template <int WT, bool BF, bool SB, bool ROWS2>
+void launch_wl(const ReduceArgs &a, dim3 grid, hipStream_t s) {
+    const int L = a.g.W / a.groups;
+    if constexpr (WT > 0) {
+        if (L == WT) {
+            hipLaunchKernelGGL((reduce_kernel<WT, WT, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a);
+            return;
+        }
+        if constexpr (WT >= 2) {
+            if (L == WT / 2) {
+                hipLaunchKernelGGL((reduce_kernel<WT, WT / 2, BF, SB, ROWS2>), grid, dim3(kThreads), 0,
+                                   s, a);
+                return;
+            }
+        }
+    }
+    hipLaunchKernelGGL((reduce_kernel<WT, 0, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a);
+}
+
 template <bool BF, bool SB, bool ROWS2>
 hipError_t launch_w(const ReduceArgs &a, dim3 grid, hipStream_t s) {
     switch (a.g.W) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<1, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<2, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<4, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<8, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((reduce_kernel<0, BF, SB, ROWS2>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: launch_wl<1, BF, SB, ROWS2>(a, grid, s); break;
+    case 2: launch_wl<2, BF, SB, ROWS2>(a, grid, s); break;
+    case 4: launch_wl<4, BF, SB, ROWS2>(a, grid, s); break;
+    case 8: launch_wl<8, BF, SB, ROWS2>(a, grid, s); break;
+    default: launch_wl<0, BF, SB, ROWS2>(a, grid, s); break;
     }
     return hipGetLastError();
 }
 
 template <bool BF, bool SB>
 hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
-    const int64_t units =
-        a.slice_kind == kSliceLastStep ? (int64_t)(a.k_hi - a.k_lo) * a.g.W * a.units_per_tile
-        : a.slice_kind == kSliceSteps  ? (int64_t)(a.k_hi - a.k_lo) * a.units_per_tile
-                                       : (int64_t)a.g.T * a.units_per_tile;
+    const int64_t units = a.slice_kind == kSliceSteps
+                              ? (int64_t)(a.k_hi - a.k_lo) * a.units_per_tile
+                              : (int64_t)a.g.T * a.units_per_tile;
     if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)units);
     // slices run beside GEMM launches: the one-row form

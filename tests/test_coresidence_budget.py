@@ -31,11 +31,28 @@ def _report(src):
         if m:
             cur = kernels.setdefault(m.group(1), {})
             continue
-        m = re.search(r"remark:\s+(VGPRs|AGPRs|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]): (\d+)",
-                      line)
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]|"
+                      r"ScratchSize \[bytes/lane\]): (\d+)", line)
         if m and cur is not None:
             cur[m.group(1).split(" ")[0]] = int(m.group(2))
     return kernels
+
+
+def _params(name):
+    """Template arguments of a gemm_bf16_kernel instantiation: BM, BN, BK,
+    STAGES, WGM, WGN and FW (0: plain epilogue, W: owner-fused reduce)."""
+    return tuple(map(int, re.search(
+        r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups()))
+
+
+def _gemms():
+    return {k: v for k, v in _report(os.path.join(B.CSRC, "gemm_bf16.hip")).items()
+            if "gemm_bf16_kernel" in k}
+
+
+def _plain_gemms():
+    # the instantiations the all-gather and the overlapped slices run beside
+    return {k: v for k, v in _gemms().items() if _params(k)[6] == 0}
 
 
 def _alloc(vgprs, agprs):
@@ -53,12 +70,10 @@ def test_copy_wave_fits_beside_every_gemm_configuration():
     assert len(copy) == 1
     copy_alloc = _alloc(copy[0]["VGPRs"], copy[0].get("AGPRs", 0))
     assert copy[0].get("LDS", 0) == 0
-    gemms = {k: v for k, v in _report(os.path.join(B.CSRC, "gemm_bf16.hip")).items()
-             if "gemm_bf16_kernel" in k}
+    gemms = _plain_gemms()
     assert len(gemms) == 4
     for name, r in gemms.items():
-        bm, bn, bk, stages, wgm, wgn = map(int, re.search(
-            r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups())
+        bm, bn, bk, stages, wgm, wgn, _ = _params(name)
         lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
         wgs_per_cu = LDS_PER_CU // lds
         waves_by_lds = -(-wgs_per_cu * wgm * wgn // SIMDS_PER_CU)
@@ -80,12 +95,27 @@ def test_overlap_reduce_slices_fit_beside_every_gemm_configuration():
            if "reduce_kernel" in k and k.endswith("ELb0EEEvNS_10ReduceArgsE")}
     assert red, "one-row reduce instantiations not found"
     need = max(_alloc(v["VGPRs"], v.get("AGPRs", 0)) for v in red.values())
-    gemms = {k: v for k, v in _report(os.path.join(B.CSRC, "gemm_bf16.hip")).items()
-             if "gemm_bf16_kernel" in k}
+    gemms = _plain_gemms()
     for name, r in gemms.items():
-        bm, bn, bk, stages, wgm, wgn = map(int, re.search(
-            r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups())
+        bm, bn, bk, stages, wgm, wgn, _ = _params(name)
         lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
         waves = min(r["Occupancy"], -(-(LDS_PER_CU // lds) * wgm * wgn // SIMDS_PER_CU))
         free = VGPRS_PER_SIMD_LANE - waves * _alloc(r["VGPRs"], r.get("AGPRs", 0))
         assert need <= free, (bm, bn, need, free)
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC),
+                    reason="hipcc not available")
+def test_fused_reduce_variant_keeps_the_plain_occupancy():
+    """The owner-fused reduce epilogue holds a row's remote partials in
+    registers: it must not spill or drop below the plain kernel's two
+    workgroup waves per SIMD."""
+    gemms = _gemms()
+    fused = {k: v for k, v in gemms.items() if _params(k)[6] > 0}
+    assert fused, "no owner-fused instantiation"
+    for name, r in fused.items():
+        plain = [v for k, v in gemms.items() if _params(k)[:6] == _params(name)[:6]
+                 and _params(k)[6] == 0]
+        assert len(plain) == 1
+        assert r.get("ScratchSize", 0) == 0, name
+        assert r["Occupancy"] >= plain[0]["Occupancy"], (name, r, plain[0])

@@ -165,11 +165,11 @@ def test_output_rounding_ties_w1():
 @pytest.mark.parametrize("name", ["llama8b", "ragged_2lvl", "decode",
                                   "llama70b_small"])
 def test_overlapped_reduce_matches_serial_bits(name, swizzle):
-    """The overlapped order (the GEMM in slices, each slice's completed
-    tiles reduced on a second stream while the next slice computes: the
-    last step's slices for the remote-first order, chunk by chunk for the
-    identity order) gives the same bits as the serial remote-first order;
-    decode has unequal chunks and takes the serial path."""
+    """The overlapped orders give the same bits as the serial remote-first
+    order: the owner-fused reduce for the remote-first order (the last
+    step's workgroups sum their tiles), chunk-by-chunk slices reduced on a
+    second stream for the identity order; decode has unequal chunks and
+    takes the serial path."""
     import torch
     if name == "llama70b_small":
         w = I.with_shape(I.WORKLOADS["llama70b"], M=2048, N=1024, K=512)
