@@ -14,30 +14,13 @@ import oracle as O
 from tensor_gemm_reduce_lds_amd import gemm_rs as G
 from tensor_gemm_reduce_lds_amd import inputs as I
 
-from gpu_util import (d2h, desc_fields, flags, geometry, h2d, hip, new_out, oracle_kw,
-                      out_bits, out_to_f64, run_checked, say, to_device)
+from gpu_util import (check_bf16_staging, d2h, desc_fields, flags, geometry, h2d, hip,
+                      new_out, oracle_kw, out_bits, out_to_f64, run_checked, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
 W70 = I.WORKLOADS
 BF = dict(staging_dtype=G.STAGING_BF16)
-
-
-def check_bf16_staging(got, ref, mag):
-    """Bar for bfloat16 staging.  Elementwise, the rounding bound: each
-    staged partial and the output are rounded to 8 significant bits, so
-    |got - ref| <= 2^-8 |ref| + 2^-8 (1 + 2^-8) sum_r |D_r|, plus 1e-4
-    sum_r |D_r| for the float accumulation and summation order.  A bound
-    relative to |ref| alone cannot hold: when the W partials cancel, their
-    rounding errors do not.  In aggregate, rel-Frobenius <= 3e-3: rounding
-    each of W independent partials to 8 bits adds about the output
-    rounding's own error (~1.7e-3 each for N(0,1) data, ~2.4e-3 together)."""
-    err = np.abs(got - ref)
-    bound = 2.0 ** -8 * np.abs(ref) + (2.0 ** -8 * (1 + 2.0 ** -8) + 1e-4) * mag + 1e-6
-    assert np.all(err <= bound), float((err / bound).max())
-    rf = O.rel_frobenius(got, ref)
-    assert rf <= 3e-3, rf
-    return float((err / bound).max()), rf
 
 
 def staging16_rows(plan, geom, d, r, il0, n):
