@@ -160,26 +160,11 @@ hipError_t clear_protocol_state(gemm_rs_plan_s *p, hipStream_t s) {
     return e;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *gemm_rs_strerror(int code) {
-    switch (code) {
-    case GEMM_RS_OK: return "ok";
-    case GEMM_RS_ERR_INVALID_ARG: return "invalid argument";
-    case GEMM_RS_ERR_UNSUPPORTED: return "unsupported configuration";
-    case GEMM_RS_ERR_HIP: return "HIP runtime error";
-    case GEMM_RS_ERR_TIMEOUT: return "device flag wait timed out";
-    case GEMM_RS_ERR_PROTOCOL: return "flag protocol violation";
-    default: return "unknown status";
-    }
-}
-
-int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
-    if (out) *out = nullptr;
-    if (!desc || !out) return GEMM_RS_ERR_INVALID_ARG;
-    gemm_rs_desc_t d = *desc;
+// Validate a descriptor, fill in its defaults and derive everything a pass
+// needs except the workspace: geometry, timeout, buffer sizes.  Makes no
+// allocation (shared by the plan and the no-allocation entry point).
+int resolve(const gemm_rs_desc_t &desc, gemm_rs_plan_s *p) {
+    gemm_rs_desc_t d = desc;
     int32_t bm = 0, bn = 0;
     pick_default_tile(d, &bm, &bn);
     int rc = validate(d, bm, bn);
@@ -192,8 +177,6 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     if (d.order == GEMM_RS_ORDER_FLAT) d.groups = 1;
     if (d.timeout_ms == 0) d.timeout_ms = 1000;
 
-    gemm_rs_plan_s *p = (gemm_rs_plan_s *)calloc(1, sizeof(gemm_rs_plan_s));
-    if (!p) return GEMM_RS_ERR_HIP;
     p->d = d;
     TileGeom &g = p->g;
     g.M = d.M; g.N = d.N; g.K = d.K; g.W = d.W; g.Mc = d.M / d.W;
@@ -210,7 +193,7 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     while ((1 << g.bm_shift) < bm) ++g.bm_shift;
     p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;
 
-    if (hipGetDevice(&p->device) != hipSuccess) { free(p); return GEMM_RS_ERR_HIP; }
+    if (hipGetDevice(&p->device) != hipSuccess) return GEMM_RS_ERR_HIP;
     int rate_khz = 0;
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate,
                               p->device) != hipSuccess || rate_khz <= 0)
@@ -222,23 +205,10 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     p->flags_bytes = (int64_t)d.W * g.T * 4;
     p->counters_bytes = (int64_t)g.T * 4;
     p->trace_bytes = (int64_t)d.W * g.T * 4;
-    hipError_t e = hipMalloc(&p->staging, p->staging_bytes);
-    if (e == hipSuccess) e = hipMalloc(&p->flags, p->flags_bytes);
-    if (e == hipSuccess) e = hipMalloc(&p->counters, p->counters_bytes);
-    if (e == hipSuccess) e = hipMalloc(&p->err, 4 * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&p->trace, p->trace_bytes);
-    if (e == hipSuccess && d.materialize_sub) {
+    if (d.materialize_sub) {
         p->sub_bytes = (int64_t)d.groups * d.M * d.N * 4;
         p->sub_flags_bytes = (int64_t)d.groups * g.T * p->units_per_tile * 4;
-        e = hipMalloc(&p->sub, p->sub_bytes);
-        if (e == hipSuccess) e = hipMalloc(&p->sub_flags, p->sub_flags_bytes);
-        if (e == hipSuccess)
-            e = hipMalloc(&p->sub_counters, p->counters_bytes * d.groups);
     }
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
-    for (int i = 0; i < kEvents && e == hipSuccess; ++i)
-        e = hipEventCreateWithFlags(&p->slice_done[i], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->aux_done, hipEventDisableTiming);
     {
         const int32_t n0 = chunk_first_tile_row(g, 1) - chunk_first_tile_row(g, 0);
         p->uniform_chunks = true;
@@ -246,54 +216,14 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
             if (chunk_first_tile_row(g, dd + 1) - chunk_first_tile_row(g, dd) != n0)
                 p->uniform_chunks = false;
     }
-    // flags are zeroed once, here; runs keep them at 0 between passes.  The
-    // zeroing runs on the plan's own stream and only that stream is waited
-    // for (unrelated work on the device is not)
-    if (e == hipSuccess) e = clear_protocol_state(p, p->aux);
-    if (e == hipSuccess) e = hipMemsetAsync(p->trace, 0xff, p->trace_bytes, p->aux);
-    if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
-    if (e != hipSuccess) {
-        free_plan(p);
-        return GEMM_RS_ERR_HIP;
-    }
-    *out = p;
     return GEMM_RS_OK;
 }
 
-int gemm_rs_destroy(gemm_rs_plan_t p) {
-    free_plan(p);
-    return GEMM_RS_OK;
-}
-
-int gemm_rs_query(gemm_rs_plan_t p, gemm_rs_info_t *info) {
-    if (!p || !info) return GEMM_RS_ERR_INVALID_ARG;
-    memset(info, 0, sizeof(*info));
-    info->Mc = p->g.Mc;
-    info->tile_m = p->g.BM;
-    info->tile_n = p->g.BN;
-    info->tiles_m = p->g.tiles_m;
-    info->tiles_n = p->g.tiles_n;
-    info->T = p->g.T;
-    info->group_m = p->g.group_m;
-    info->staging = p->staging;
-    info->flags = p->flags;
-    info->sub = p->sub;
-    info->sub_flags = p->sub_flags;
-    info->trace = p->trace;
-    info->staging_bytes = p->staging_bytes;
-    info->flags_bytes = p->flags_bytes;
-    info->sub_bytes = p->sub_bytes;
-    info->sub_flags_bytes = p->sub_flags_bytes;
-    info->workspace_bytes = p->staging_bytes + p->flags_bytes +
-                            p->counters_bytes * (1 + (p->sub_counters ? p->d.groups : 0)) +
-                            p->sub_bytes + p->sub_flags_bytes + p->trace_bytes + 16;
-    return GEMM_RS_OK;
-}
-
-int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
-                float alpha, float beta, void *out, void *stream,
-                uint32_t run_flags) {
-    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
+// Enqueue one pass of plan p on stream s (checks the run flags and
+// pointers, no host synchronisation, no allocation).  Without an auxiliary
+// stream (p->aux == nullptr) the identity-order overlap runs serially.
+int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, float alpha,
+            float beta, void *out, hipStream_t s, uint32_t run_flags) {
     const uint32_t known = GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE |
                            GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES |
                            GEMM_RS_OVERLAP_REDUCE;
@@ -308,7 +238,6 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         if (!p->d.has_c && C) return GEMM_RS_ERR_INVALID_ARG;
     }
     if (do_reduce && (!out || !aligned16(out))) return GEMM_RS_ERR_INVALID_ARG;
-    hipStream_t s = (hipStream_t)stream;
 
     GemmArgs a = {};   // fields this path does not use stay zero (no gate, no plain output)
     a.g = p->g;
@@ -362,7 +291,7 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
                        p->d.dtype == GEMM_RS_BF16 && !(run_flags & GEMM_RS_KEEP_FLAGS) &&
                        fused_reduce_supported(p->g.BM, p->g.BN, p->g.W);
     // identity order: chunk-by-chunk slices reduced on the second stream
-    const bool sliced = overlap_req && p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY;
+    const bool sliced = overlap_req && p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY && p->aux;
     hipError_t e = hipSuccess;
     if (fused) {
         // Every rank visits its own chunk last, so rank d's last n = T/W
@@ -427,6 +356,100 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
         }
     }
     return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_rs_strerror(int code) {
+    switch (code) {
+    case GEMM_RS_OK: return "ok";
+    case GEMM_RS_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_RS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GEMM_RS_ERR_HIP: return "HIP runtime error";
+    case GEMM_RS_ERR_TIMEOUT: return "device flag wait timed out";
+    case GEMM_RS_ERR_PROTOCOL: return "flag protocol violation";
+    default: return "unknown status";
+    }
+}
+
+int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
+    if (out) *out = nullptr;
+    if (!desc || !out) return GEMM_RS_ERR_INVALID_ARG;
+    gemm_rs_plan_s *p = (gemm_rs_plan_s *)calloc(1, sizeof(gemm_rs_plan_s));
+    if (!p) return GEMM_RS_ERR_HIP;
+    const int rc = resolve(*desc, p);
+    if (rc != GEMM_RS_OK) {
+        free(p);
+        return rc;
+    }
+    const gemm_rs_desc_t &d = p->d;
+    hipError_t e = hipMalloc(&p->staging, p->staging_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->flags, p->flags_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->counters, p->counters_bytes);
+    if (e == hipSuccess) e = hipMalloc(&p->err, 4 * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&p->trace, p->trace_bytes);
+    if (e == hipSuccess && d.materialize_sub) {
+        e = hipMalloc(&p->sub, p->sub_bytes);
+        if (e == hipSuccess) e = hipMalloc(&p->sub_flags, p->sub_flags_bytes);
+        if (e == hipSuccess)
+            e = hipMalloc(&p->sub_counters, p->counters_bytes * d.groups);
+    }
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
+    for (int i = 0; i < kEvents && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&p->slice_done[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->aux_done, hipEventDisableTiming);
+    // flags are zeroed once, here; runs keep them at 0 between passes.  The
+    // zeroing runs on the plan's own stream and only that stream is waited
+    // for (unrelated work on the device is not)
+    if (e == hipSuccess) e = clear_protocol_state(p, p->aux);
+    if (e == hipSuccess) e = hipMemsetAsync(p->trace, 0xff, p->trace_bytes, p->aux);
+    if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
+    if (e != hipSuccess) {
+        free_plan(p);
+        return GEMM_RS_ERR_HIP;
+    }
+    *out = p;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_destroy(gemm_rs_plan_t p) {
+    free_plan(p);
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_query(gemm_rs_plan_t p, gemm_rs_info_t *info) {
+    if (!p || !info) return GEMM_RS_ERR_INVALID_ARG;
+    memset(info, 0, sizeof(*info));
+    info->Mc = p->g.Mc;
+    info->tile_m = p->g.BM;
+    info->tile_n = p->g.BN;
+    info->tiles_m = p->g.tiles_m;
+    info->tiles_n = p->g.tiles_n;
+    info->T = p->g.T;
+    info->group_m = p->g.group_m;
+    info->staging = p->staging;
+    info->flags = p->flags;
+    info->sub = p->sub;
+    info->sub_flags = p->sub_flags;
+    info->trace = p->trace;
+    info->staging_bytes = p->staging_bytes;
+    info->flags_bytes = p->flags_bytes;
+    info->sub_bytes = p->sub_bytes;
+    info->sub_flags_bytes = p->sub_flags_bytes;
+    info->workspace_bytes = p->staging_bytes + p->flags_bytes +
+                            p->counters_bytes * (1 + (p->sub_counters ? p->d.groups : 0)) +
+                            p->sub_bytes + p->sub_flags_bytes + p->trace_bytes + 16;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
+                float alpha, float beta, void *out, void *stream,
+                uint32_t run_flags) {
+    if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
+    return enqueue(p, A, B, C, alpha, beta, out, (hipStream_t)stream, run_flags);
 }
 
 int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {
