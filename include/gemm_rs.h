@@ -54,6 +54,8 @@ extern "C" {
 #define GEMM_RS_ERR_HIP       (-3)  /* a HIP call failed (alloc / launch)    */
 #define GEMM_RS_ERR_TIMEOUT   (-4)  /* async: a flag wait ran out of time    */
 #define GEMM_RS_ERR_PROTOCOL  (-5)  /* async: a flag held neither 0 nor 1    */
+#define GEMM_RS_ERR_SCRATCH   (-6)  /* gemm_rs_run_noalloc: the workspace
+                                       exceeds its static scratch          */
 
 /* ---- descriptor enums -------------------------------------------------- */
 #define GEMM_RS_BF16 0 /* A, B, C bfloat16; out bfloat16 (RNE); fp32 accumulate */
@@ -224,6 +226,38 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
 GEMM_RS_API int gemm_rs_run(gemm_rs_plan_t plan, const void *A, const void *B,
                 const void *C, float alpha, float beta, void *out,
                 void *stream, uint32_t run_flags);
+
+/*
+ * gemm_rs_run_noalloc: gemm_rs_run without a plan and without allocating,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * validates *desc as gemm_rs_plan does and enqueues one whole pass on
+ * `stream` with the same kernels, keeping the workspace (error record,
+ * flags, counters, staging) in one static device array of 64 MiB per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * No hipMalloc, hipFree, stream or event creation, and no host
+ * synchronisation.
+ *   desc, A, B, C, alpha, beta, out, stream: as for gemm_rs_plan and
+ *        gemm_rs_run (pointers are caller-owned device memory)
+ *   run_flags  GEMM_RS_RUN_ALL, optionally | GEMM_RS_OVERLAP_REDUCE (the
+ *        owner-fused reduce where gemm_rs_run would use it; the identity
+ *        order's second-stream overlap runs serially here).  Split passes
+ *        and the debug bits are INVALID_ARG: the flags are cleared at the
+ *        start of every call.
+ *   status  NULL, or 4 int32 of 16-byte-aligned device memory: zeroed at
+ *        the start of the pass, then {code, rank, tile, value} of the first
+ *        asynchronous error (TIMEOUT or PROTOCOL) of the pass
+ * Returns OK, INVALID_ARG / UNSUPPORTED (as gemm_rs_plan; materialize_sub
+ * is UNSUPPORTED here), SCRATCH when the workspace (256 bytes + W*T*4 +
+ * T*4, each rounded up to 256, + W*M*N*4 staging bytes, *2 with bfloat16
+ * staging) exceeds 64 MiB, or HIP.  Every call on one GPU shares the same
+ * array: calls that overlap on one GPU (two streams, or two threads) race
+ * and give undefined results; calls ordered on one stream are safe.
+ */
+GEMM_RS_API int gemm_rs_run_noalloc(const gemm_rs_desc_t *desc, const void *A,
+                                    const void *B, const void *C, float alpha,
+                                    float beta, void *out, void *stream,
+                                    uint32_t run_flags, int32_t *status);
 
 /*
  * gemm_rs_destroy: free the workspace.  The caller must synchronise every

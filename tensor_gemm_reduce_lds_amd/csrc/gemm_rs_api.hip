@@ -6,10 +6,16 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemm_rs.h"
 #include "gemm_rs_internal.h"
 
 using namespace gemm_rs;
+
+// Workspace of gemm_rs_run_noalloc (see device_scratch below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // overlapped reduce with the identity order: at most this many chunk groups
 constexpr int kChunkSlices = 8;
@@ -160,8 +166,8 @@ hipError_t clear_protocol_state(gemm_rs_plan_s *p, hipStream_t s) {
     return e;
 }
 
-// Validate a descriptor, fill in its defaults and derive everything a pass
-// needs except the workspace: geometry, timeout, buffer sizes.  Makes no
+// Validate a descriptor, fill in its defaults and derive the geometry and
+// buffer sizes of a pass.  Host arithmetic only: no HIP call, no
 // allocation (shared by the plan and the no-allocation entry point).
 int resolve(const gemm_rs_desc_t &desc, gemm_rs_plan_s *p) {
     gemm_rs_desc_t d = desc;
@@ -193,13 +199,6 @@ int resolve(const gemm_rs_desc_t &desc, gemm_rs_plan_s *p) {
     while ((1 << g.bm_shift) < bm) ++g.bm_shift;
     p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;
 
-    if (hipGetDevice(&p->device) != hipSuccess) return GEMM_RS_ERR_HIP;
-    int rate_khz = 0;
-    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate,
-                              p->device) != hipSuccess || rate_khz <= 0)
-        rate_khz = 100000;  // the 100 MHz constant clock
-    p->timeout_ticks = (uint64_t)d.timeout_ms * (uint64_t)rate_khz;
-
     p->staging_bytes =
         (int64_t)d.W * d.M * d.N * (d.staging_dtype == GEMM_RS_STAGING_BF16 ? 2 : 4);
     p->flags_bytes = (int64_t)d.W * g.T * 4;
@@ -216,6 +215,17 @@ int resolve(const gemm_rs_desc_t &desc, gemm_rs_plan_s *p) {
             if (chunk_first_tile_row(g, dd + 1) - chunk_first_tile_row(g, dd) != n0)
                 p->uniform_chunks = false;
     }
+    return GEMM_RS_OK;
+}
+
+// The current device and the flag-wait bound in its wall-clock ticks.
+int resolve_device(gemm_rs_plan_s *p) {
+    if (hipGetDevice(&p->device) != hipSuccess) return GEMM_RS_ERR_HIP;
+    int rate_khz = 0;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate,
+                              p->device) != hipSuccess || rate_khz <= 0)
+        rate_khz = 100000;  // the 100 MHz constant clock
+    p->timeout_ticks = (uint64_t)p->d.timeout_ms * (uint64_t)rate_khz;
     return GEMM_RS_OK;
 }
 
@@ -359,6 +369,33 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
 }
 
 
+// ---- workspace of the no-allocation entry point ----
+// One static device array: every GPU the library runs on holds its own copy
+// until the process ends, and every gemm_rs_run_noalloc call on that GPU
+// shares it.  In host code the array's name is not a device address; the
+// address comes from hipGetSymbolAddress, once per device, and only that
+// pointer is handed to kernels.
+constexpr int kMaxScratchDevices = 64;
+std::once_flag scratch_once[kMaxScratchDevices];
+void *scratch_ptr[kMaxScratchDevices];
+hipError_t scratch_rc[kMaxScratchDevices];
+
+// The current device's copy of the scratch array (looked up on the first
+// call made with that device current).
+hipError_t device_scratch(int dev, unsigned char **ptr) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(scratch_once[dev], [dev] {
+        void *q = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        scratch_rc[dev] = e;
+        scratch_ptr[dev] = e == hipSuccess ? q : nullptr;
+    });
+    *ptr = (unsigned char *)scratch_ptr[dev];
+    return scratch_rc[dev];
+}
+
+int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +408,8 @@ const char *gemm_rs_strerror(int code) {
     case GEMM_RS_ERR_HIP: return "HIP runtime error";
     case GEMM_RS_ERR_TIMEOUT: return "device flag wait timed out";
     case GEMM_RS_ERR_PROTOCOL: return "flag protocol violation";
+    case GEMM_RS_ERR_SCRATCH:
+        return "workspace larger than the static scratch of gemm_rs_run_noalloc";
     default: return "unknown status";
     }
 }
@@ -380,7 +419,8 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     if (!desc || !out) return GEMM_RS_ERR_INVALID_ARG;
     gemm_rs_plan_s *p = (gemm_rs_plan_s *)calloc(1, sizeof(gemm_rs_plan_s));
     if (!p) return GEMM_RS_ERR_HIP;
-    const int rc = resolve(*desc, p);
+    int rc = resolve(*desc, p);
+    if (rc == GEMM_RS_OK) rc = resolve_device(p);
     if (rc != GEMM_RS_OK) {
         free(p);
         return rc;
@@ -450,6 +490,42 @@ int gemm_rs_run(gemm_rs_plan_t p, const void *A, const void *B, const void *C,
                 uint32_t run_flags) {
     if (!p || !on_plan_device(p->device)) return GEMM_RS_ERR_INVALID_ARG;
     return enqueue(p, A, B, C, alpha, beta, out, (hipStream_t)stream, run_flags);
+}
+
+int gemm_rs_run_noalloc(const gemm_rs_desc_t *desc, const void *A, const void *B,
+                        const void *C, float alpha, float beta, void *out, void *stream,
+                        uint32_t run_flags, int32_t *status) {
+    if (!desc) return GEMM_RS_ERR_INVALID_ARG;
+    const uint32_t allowed = GEMM_RS_RUN_ALL | GEMM_RS_OVERLAP_REDUCE;
+    if ((run_flags & GEMM_RS_RUN_ALL) != GEMM_RS_RUN_ALL || (run_flags & ~allowed))
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (status && ((uintptr_t)status & 15u)) return GEMM_RS_ERR_INVALID_ARG;
+    gemm_rs_plan_s p;
+    memset(&p, 0, sizeof p);
+    int rc = resolve(*desc, &p);
+    if (rc != GEMM_RS_OK) return rc;
+    if (p.d.materialize_sub) return GEMM_RS_ERR_UNSUPPORTED;
+    // layout: error record | flags [W][T] | counters [T] | staging
+    const int64_t off_flags = 256;
+    const int64_t off_counters = off_flags + align256(p.flags_bytes);
+    const int64_t off_staging = off_counters + align256(p.counters_bytes);
+    if (off_staging + p.staging_bytes > (int64_t)kScratchBytes) return GEMM_RS_ERR_SCRATCH;
+    rc = resolve_device(&p);
+    if (rc != GEMM_RS_OK) return rc;
+    unsigned char *base = nullptr;
+    if (device_scratch(p.device, &base) != hipSuccess || !base) return GEMM_RS_ERR_HIP;
+    p.err = status ? status : (int32_t *)base;
+    p.flags = (uint32_t *)(base + off_flags);
+    p.counters = (uint32_t *)(base + off_counters);
+    p.staging = base + off_staging;
+    hipStream_t s = (hipStream_t)stream;
+    // the array keeps the previous call's contents: flags, counters and
+    // the error record start every call at zero (flags and counters are
+    // one contiguous range)
+    const hipError_t e =
+        launch_clear_words(p.flags, (off_staging - off_flags) / 4, (uint32_t *)p.err, 4, s);
+    if (e != hipSuccess) return GEMM_RS_ERR_HIP;
+    return enqueue(&p, A, B, C, alpha, beta, out, s, run_flags);
 }
 
 int gemm_rs_tile_order(gemm_rs_plan_t p, int32_t *host_trace) {

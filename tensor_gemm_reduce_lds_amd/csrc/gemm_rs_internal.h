@@ -255,6 +255,8 @@ hipError_t launch_reduce(const ReduceArgs &a, int dtype, hipStream_t s);
 hipError_t launch_reduce_sub(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_reduce_final_sub(const ReduceArgs &a, int dtype, hipStream_t s);
 hipError_t launch_tile_order(const TileGeom &g, int32_t *trace, hipStream_t s);
+hipError_t launch_clear_words(uint32_t *a, int64_t na, uint32_t *b, int64_t nb,
+                              hipStream_t s);
 
 // Supported bf16 tile shapes (tile_m, tile_n).
 bool bf16_tile_supported(int32_t bm, int32_t bn);

@@ -311,6 +311,14 @@ __global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a
     }
 }
 
+// Zero two word ranges (flags and counters, and an error record) with a
+// kernel rather than a memset, so the enqueue stays capturable in a graph.
+__global__ void clear_words_kernel(uint32_t *a, int64_t na, uint32_t *b, int64_t nb) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < na) a[i] = 0u;
+    else if (i < na + nb) b[i - na] = 0u;
+}
+
 __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= (int64_t)g.W * g.T) return;
@@ -387,6 +395,15 @@ hipError_t launch_reduce_final_sub(const ReduceArgs &a, int dtype, hipStream_t s
         hipLaunchKernelGGL((reduce_final_sub_kernel<true>), grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((reduce_final_sub_kernel<false>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_words(uint32_t *a, int64_t na, uint32_t *b, int64_t nb,
+                              hipStream_t s) {
+    const int64_t n = na + nb;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a, na, b, nb);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ ERR_UNSUPPORTED = -2
 ERR_HIP = -3
 ERR_TIMEOUT = -4
 ERR_PROTOCOL = -5
+ERR_SCRATCH = -6
 
 BF16, F32 = 0, 1
 ORDER_FLAT, ORDER_TWO_LEVEL = 0, 1
@@ -106,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gemm_rs_plan.argtypes = [ctypes.POINTER(gemm_rs_desc_t), ctypes.POINTER(vp)]
     lib.gemm_rs_run.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                 vp, vp, u32]
+    lib.gemm_rs_run_noalloc.argtypes = [ctypes.POINTER(gemm_rs_desc_t), vp, vp, vp,
+                                        ctypes.c_float, ctypes.c_float, vp, vp, u32, vp]
     lib.gemm_rs_destroy.argtypes = [vp]
     lib.gemm_rs_query.argtypes = [vp, ctypes.POINTER(gemm_rs_info_t)]
     lib.gemm_rs_tile_order.argtypes = [vp, vp]
@@ -117,7 +120,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gemm_ag_query.argtypes = [vp, ctypes.POINTER(gemm_ag_info_t)]
     lib.gemm_ag_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gemm_ag_destroy.argtypes = [vp]
-    for f in ("gemm_rs_plan", "gemm_rs_run", "gemm_rs_destroy", "gemm_rs_query",
+    for f in ("gemm_rs_plan", "gemm_rs_run", "gemm_rs_run_noalloc", "gemm_rs_destroy",
+              "gemm_rs_query",
               "gemm_rs_tile_order", "gemm_rs_status", "gemm_ag_plan", "gemm_ag_run",
               "gemm_ag_query", "gemm_ag_status", "gemm_ag_destroy"):
         getattr(lib, f).restype = ctypes.c_int
@@ -180,6 +184,13 @@ def gemm_rs_plan(desc: Optional[gemm_rs_desc_t]):
 def gemm_rs_run(plan, A, B, C, alpha, beta, out, stream=None, run_flags=RUN_ALL) -> int:
     return load_library().gemm_rs_run(plan, _ptr(A), _ptr(B), _ptr(C), alpha, beta,
                                       _ptr(out), _stream_handle(stream), run_flags)
+
+
+def gemm_rs_run_noalloc(desc: Optional[gemm_rs_desc_t], A, B, C, alpha, beta, out,
+                        stream=None, run_flags=RUN_ALL, status=None) -> int:
+    return load_library().gemm_rs_run_noalloc(
+        None if desc is None else ctypes.byref(desc), _ptr(A), _ptr(B), _ptr(C), alpha, beta,
+        _ptr(out), _stream_handle(stream), run_flags, _ptr(status))
 
 
 def gemm_rs_destroy(plan) -> int:

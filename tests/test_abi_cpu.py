@@ -16,7 +16,8 @@ F32_TILES = [(64, 64)]
 
 def test_library_exports_every_header_function():
     names = G.header_functions()
-    assert names == sorted(["gemm_rs_plan", "gemm_rs_run", "gemm_rs_destroy",
+    assert names == sorted(["gemm_rs_plan", "gemm_rs_run", "gemm_rs_run_noalloc",
+                            "gemm_rs_destroy",
                             "gemm_rs_query", "gemm_rs_tile_order",
                             "gemm_rs_status", "gemm_rs_strerror",
                             "gemm_ag_plan", "gemm_ag_run", "gemm_ag_query",
@@ -119,3 +120,30 @@ def test_bad_ag_descriptors_rejected_like_oracle(kw):
     assert want != O.OK
     rc, h = G.gemm_ag_plan(G.make_ag_desc(**base))
     assert rc == want and h is None
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """gemm_rs_run_noalloc checks its descriptor, flags and workspace size
+    on the host before it touches a device."""
+    assert G.gemm_rs_run_noalloc(None, None, None, None, 1.0, 0.0, None) == G.ERR_INVALID_ARG
+    base = dict(M=64, N=1024, K=512, W=8, dtype=0, tile_m=64, tile_n=128)
+    for kw in BAD[:10]:
+        d = dict(base, **kw)
+        tiles = F32_TILES if d["dtype"] == 1 else BF16_TILES
+        want = O.validate(**d, supported_tiles=tiles)
+        assert G.gemm_rs_run_noalloc(G.make_desc(**d), None, None, None, 1.0, 0.0,
+                                     None) == want, kw
+    # the 70B-like shard's 2 GiB of staging does not fit in 64 MiB
+    big = G.make_desc(M=8192, N=8192, K=3584, W=8)
+    assert G.gemm_rs_run_noalloc(big, None, None, None, 1.0, 0.0, None) == G.ERR_SCRATCH
+    # 64 MiB holds W*M*N*4 = 8*256*8192*4 = 64 MiB only without the flag words
+    edge = G.make_desc(M=256, N=8192, K=64, W=8)
+    assert G.gemm_rs_run_noalloc(edge, None, None, None, 1.0, 0.0, None) == G.ERR_SCRATCH
+    sub = G.make_desc(M=64, N=1024, K=64, W=8, order=1, groups=2, materialize_sub=1)
+    assert G.gemm_rs_run_noalloc(sub, None, None, None, 1.0, 0.0, None) == G.ERR_UNSUPPORTED
+    d = G.make_desc(**base)
+    for flags in (G.RUN_GEMM, G.RUN_REDUCE, G.RUN_ALL | G.KEEP_FLAGS, G.RUN_ALL | G.TRACE_TILES,
+                  G.RUN_ALL | 64):
+        assert G.gemm_rs_run_noalloc(d, None, None, None, 1.0, 0.0, None, None,
+                                     flags) == G.ERR_INVALID_ARG, flags
+    assert G.gemm_rs_strerror(G.ERR_SCRATCH).startswith("workspace larger than")
