@@ -416,13 +416,13 @@ def main():
     # rank's own-chunk step sums its tiles' partials in its epilogue, no
     # separate reduce); identity order (a second plan): chunk c's reduce
     # overlaps the GEMM of chunk c+1 on the plan's second stream.
-    def overlapped_ms(p):
+    def overlapped_ms(p, flags=G.RUN_ALL | G.OVERLAP_REDUCE):
         for _ in range(2):
-            p.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+            p.run(A, B, C, w.alpha, w.beta, out, stream, flags)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(args.steps):
-            p.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+            p.run(A, B, C, w.alpha, w.beta, out, stream, flags)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t1) * 1e3 / args.steps
         rc, detail = p.status(stream)
@@ -430,9 +430,10 @@ def main():
             raise RuntimeError("overlapped run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
         return ms
 
-    ov_ms = ov_id_ms = None
+    ov_ms = ov_id_ms = la_ms = None
     if not args.no_overlap:
         ov_ms = overlapped_ms(plan)
+        la_ms = overlapped_ms(plan, G.RUN_ALL | G.LAST_ARRIVER)
         with G.Plan(**dict(plan_fields, swizzle=G.SWIZZLE_IDENTITY)) as plan_id:
             ov_id_ms = overlapped_ms(plan_id)
 
@@ -546,6 +547,10 @@ def main():
                                         else round((gemm_ms + red_ms - ov_id_ms) / red_ms, 3)),
         "value_overlap_identity": (None if ov_id_ms is None
                                    else round(flops / (ov_id_ms * 1e-3) / 1e12, 2)),
+        # one launch, each tile summed by its last producer (agent-scope
+        # release per producer, acquire per summing workgroup)
+        "ms_per_step_last_arriver": None if la_ms is None else round(la_ms, 4),
+        "value_last_arriver": None if la_ms is None else round(flops / (la_ms * 1e-3) / 1e12, 2),
         "bf16_staging": bf16_staging,
         "ablation": ablation,
         "ag_gemm": ag_gemm,

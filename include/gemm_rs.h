@@ -85,6 +85,9 @@ extern "C" {
 #define GEMM_RS_OVERLAP_REDUCE 16u /* with RUN_GEMM|RUN_REDUCE: take the reduce
                                       off the serial path (owner-fused or
                                       overlapped; see gemm_rs_run) */
+#define GEMM_RS_LAST_ARRIVER 32u /* with RUN_GEMM|RUN_REDUCE: one launch, each
+                                    tile summed by its last producer (see
+                                    gemm_rs_run) */
 #define GEMM_RS_RUN_ALL     (GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE)
 
 /*
@@ -216,6 +219,19 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
  *     after each, an auxiliary stream owned by the plan reduces the chunks
  *     it completed, concurrently with the next group; `stream` waits for
  *     the auxiliary stream at the end.
+ * GEMM_RS_LAST_ARRIVER (both RUN bits; bf16, 256x256 tiles, W = 8, flat or
+ * register two-level reduce; not with OVERLAP_REDUCE, which is
+ * INVALID_ARG; otherwise the serial path): the whole pass is one GEMM
+ * launch in any tile order.  Every producer stages its partial, publishes
+ * its tile flag after an agent-scope release (its stores written back past
+ * its XCD's L2) and counts itself in on the tile's counter with an
+ * agent-scope acquire-release add.  The producer that completes the count
+ * (page "flux实现：sm80 gemm+rs", section "device side barrier": the
+ * counter whose last arrival ends the wait) checks and resets the tile's
+ * flags and counter and sums the tile's W partials in the reduce order
+ * (its own from registers) into `out`.  No workgroup waits for another,
+ * so it cannot deadlock whatever the residency; each producer pays the
+ * release.
  * Results are bit-identical to the serial order.
  * The caller owns A, B, C, out and the stream, and keeps them alive until
  * the stream's work is done.  Calls on one stream are ordered; one plan
@@ -241,7 +257,8 @@ GEMM_RS_API int gemm_rs_run(gemm_rs_plan_t plan, const void *A, const void *B,
  *        gemm_rs_run (pointers are caller-owned device memory)
  *   run_flags  GEMM_RS_RUN_ALL, optionally | GEMM_RS_OVERLAP_REDUCE (the
  *        owner-fused reduce where gemm_rs_run would use it; the identity
- *        order's second-stream overlap runs serially here).  Split passes
+ *        order's second-stream overlap runs serially here) or
+ *        | GEMM_RS_LAST_ARRIVER.  Split passes
  *        and the debug bits are INVALID_ARG: the flags are cleared at the
  *        start of every call.
  *   status  NULL, or 4 int32 of 16-byte-aligned device memory: zeroed at

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         b_voff[i] = (uint32_t)(((int64_t)k * g.N + ((lane % CPR) ^ swb(k)) * 8) * 2);
     }
 
-    auto issue = [&](int kt, int buf) {
+    auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
         const uint32_t As = smem_base + buf * STAGE;
         const uint32_t Bs = As + A_BYTES;
         const i32x4_t a_rsrc = buffer_rsrc(A + row0 * g.K + (int64_t)kt * BK, a_bytes);
@@ -237,7 +237,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto load_frags = [&](lds_char *S, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) {
+    auto load_frags = [&](lds_char *S, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN])
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(S + a_off[i][ks]);
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int KS = BK / 16;
     static_assert(KS % 2 == 0, "the last slice uses fragment buffer 1");
     bf16x8_t af[2][FM], bfr[2][FN];
-    auto mfmas = [&](int fb) {
+    auto mfmas = [&](int fb) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
     };
-    auto interleave = [&] {
+    auto interleave = [&]() __attribute__((always_inline)) {
         // schedule: one LDS read (mask 0x100), one MFMA (0x008), ...
 #pragma unroll
         for (int k = 0; k < FM + 2 * FN; ++k) {
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < KT) issue(s, s);
-    if constexpr (FW > 0) {
+    if constexpr (FW > 0) if (a.fuse_reduce == kFuseOwner) {
         // owner-fused reduce: every other rank's partial of this tile was
         // staged by an earlier launch on the stream (so it is visible
         // here); its flag must read 1.  Checked while the first operand
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         int failed = 0;
         if (tid < FW && tid != r)
             failed = wait_flag_set(a.flags + (int64_t)tid * g.T + t, a.timeout_ticks, a.err,
-                                   tid, t, false);
+                                   tid, t);
         if (__syncthreads_or(failed)) {
             wait_vmcnt<0>();                        // no DMA into LDS after exit
             return;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // its stores).  Each mode is separate code: a C load issued behind
     // stores would have to wait for all of them (memory operations complete
     // in order), so no load sits between two stores.
-    auto epilogue = [&](auto mode_tag) {
+    auto epilogue = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
         uint2 cb_row = {0u, 0u};
         float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // the bias row's 4 columns, widened
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // never staged.  The stripes pass through LDS as in the plain epilogue,
     // so a lane holds 4 consecutive columns of one row, the layout of the
     // staging slots.  Loads run one row ahead of the adds and stores.
-    auto fused_epilogue = [&](auto mode_tag, auto sb_tag) {
+    auto fused_epilogue = [&](auto mode_tag, auto sb_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
         constexpr bool SB = decltype(sb_tag)::value;
         constexpr int NR = FW > 1 ? FW - 1 : 1;      // remote partials per element
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             if (i + 1 < FM) lds_barrier();          // the stripe buffer is reused
         }
     };
-    if constexpr (FW > 0) {
+    auto run_fused_epilogue = [&]() __attribute__((always_inline)) {
         if (a.staging_bf16) {
             if (!a.has_c) fused_epilogue(std::integral_constant<int, 0>{}, std::true_type{});
             else if (a.ldc == 0) fused_epilogue(std::integral_constant<int, 1>{}, std::true_type{});
@@ -657,35 +658,82 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             else if (a.ldc == 0) fused_epilogue(std::integral_constant<int, 1>{}, std::false_type{});
             else fused_epilogue(std::integral_constant<int, 2>{}, std::false_type{});
         }
+    };
+    // the owner-fused workgroup goes straight to the fused epilogue; every
+    // other one stages its partial and publishes it (one call site of each
+    // epilogue, so both stay inlined)
+    bool fused_now = false;
+    if constexpr (FW > 0) fused_now = a.fuse_reduce == kFuseOwner;
+    if (!fused_now) {
+        if (!a.has_c) epilogue(std::integral_constant<int, 0>{});
+        else if (a.ldc == 0) epilogue(std::integral_constant<int, 1>{});
+        else epilogue(std::integral_constant<int, 2>{});
+
+        // ---- publish: all stores of this tile, then flag[r][t] = 1 ----
+        // With a consumer in the same launch (the last-arriver reduce) the flag
+        // follows an agent-scope release: the tile's stores are written back
+        // past this XCD's L2 before it.  When the consumer is stream-ordered
+        // after this kernel, the kernel boundary already makes the stores
+        // visible and the flag is a plain store.
+        if (!a.flags) {
+            // all-gather mode: an ordinary output tile, no flag
+        } else if (a.release_flags) {
+            __syncthreads();                            // every wave's stores are done
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            // the consumer runs after this kernel has completed, so the flag
+            // needs no ordering against the other waves' stores here
+            if (tid == 0)
+                __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (tid == 0 && a.trace) a.trace[b] = t;
-        return;
-    }
 
-    if (!a.has_c) epilogue(std::integral_constant<int, 0>{});
-    else if (a.ldc == 0) epilogue(std::integral_constant<int, 1>{});
-    else epilogue(std::integral_constant<int, 2>{});
-
-    // ---- publish: all stores of this tile, then flag[r][t] = 1 ----
-    // With a concurrent consumer the flag is an agent-scope release (the
-    // tile's stores are written back past this XCD's L2 first).  When the
-    // consumer is stream-ordered after this kernel, the kernel boundary
-    // already makes the stores visible and the flag is a plain store.
-    if (!a.flags) {
-        // all-gather mode: an ordinary output tile, no flag
-    } else if (a.release_flags) {
-        __threadfence();
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        // the consumer runs after this kernel has completed, so the flag
-        // needs no ordering against the other waves' stores here
-        if (tid == 0)
-            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        // ---- last-arriver reduce ----
+        // Each producer counts itself in on the tile's counter (an agent-scope
+        // acquire-release add, after its flag); the one that completes the
+        // count is the tile's last producer, so every partial of the tile is
+        // staged and released.  It takes the acquire, checks and resets the
+        // tile's W flags and the counter, and sums the tile as the owner-fused
+        // epilogue does (its own partial from registers).  No workgroup ever
+        // waits for another, so residency cannot deadlock it.
+        if constexpr (FW > 0) if (a.fuse_reduce == kFuseLastArriver) {
+            int last = 0;
+            if (tid == 0) {
+                const uint32_t old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_ACQ_REL,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                if (old == (uint32_t)FW - 1) last = 1;
+                else if (old >= (uint32_t)FW) record_error(a.err, GEMM_RS_ERR_PROTOCOL, r, t, old);
+            }
+            if (!__syncthreads_or(last)) return;
+            int bad = 0;
+            if (tid < FW) {
+                const uint32_t v = __hip_atomic_load(&a.flags[(int64_t)tid * g.T + t],
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v != 1u) {
+                    record_error(a.err, GEMM_RS_ERR_PROTOCOL, tid, t, v);
+                    bad = 1;
+                }
+            }
+            if (__syncthreads_or(bad)) return;
+            if (tid < FW && !a.keep_flags)
+                __hip_atomic_store(&a.flags[(int64_t)tid * g.T + t], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0)
+                __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fused_now = true;
+        }
     }
-    if (tid == 0 && a.trace) a.trace[b] = t;
+    if constexpr (FW > 0) {
+        if (fused_now) {
+            run_fused_epilogue();
+            if (tid == 0 && a.trace && a.fuse_reduce == kFuseOwner) a.trace[b] = t;
+        }
+    }
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW = 0>

@@ -77,17 +77,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         __builtin_nontemporal_store(x, dst + col);
     }
 
-    // flag publish: agent-scope release for a concurrent consumer, a plain
-    // store when the consumer is stream-ordered after this kernel
-    if (a.release_flags) __threadfence();
-    __syncthreads();
+    // flag publish: the consumer (the reduce) is stream-ordered after this
+    // kernel, whose boundary makes the stores visible, so the flag is a
+    // plain store
     if (tid == 0) {
-        if (a.release_flags)
-            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        else
-            __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         if (a.trace) a.trace[b] = t;
     }
 }

@@ -236,8 +236,10 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
             float beta, void *out, hipStream_t s, uint32_t run_flags) {
     const uint32_t known = GEMM_RS_RUN_GEMM | GEMM_RS_RUN_REDUCE |
                            GEMM_RS_KEEP_FLAGS | GEMM_RS_TRACE_TILES |
-                           GEMM_RS_OVERLAP_REDUCE;
+                           GEMM_RS_OVERLAP_REDUCE | GEMM_RS_LAST_ARRIVER;
     if (run_flags & ~known) return GEMM_RS_ERR_INVALID_ARG;
+    if ((run_flags & GEMM_RS_OVERLAP_REDUCE) && (run_flags & GEMM_RS_LAST_ARRIVER))
+        return GEMM_RS_ERR_INVALID_ARG;
     const bool do_gemm = run_flags & GEMM_RS_RUN_GEMM;
     const bool do_reduce = run_flags & GEMM_RS_RUN_REDUCE;
     if (do_gemm) {
@@ -259,8 +261,9 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
     a.staging_bf16 = p->d.staging_dtype == GEMM_RS_STAGING_BF16;
     a.flags = p->flags;
     a.trace = (run_flags & GEMM_RS_TRACE_TILES) ? p->trace : nullptr;
-    // every consumer runs after the producing launch completes (same stream
-    // or an event dependency), so flags are published with plain stores
+    // consumers run after the producing launch completes (same stream or an
+    // event dependency), so flags are published with plain stores; only the
+    // last-arriver mode (a consumer in the same launch) releases them
     a.release_flags = 0;
     a.b_offset = 0;
     a.n_blocks = (uint32_t)((int64_t)p->g.W * p->g.T);
@@ -280,7 +283,6 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
     r.order = p->d.order;
     r.groups = p->d.groups;
     r.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
-    r.acquire = 0;
     r.units_per_tile = p->units_per_tile;
     r.timeout_ticks = p->timeout_ticks;
     r.staging = p->staging;
@@ -302,7 +304,23 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
                        fused_reduce_supported(p->g.BM, p->g.BN, p->g.W);
     // identity order: chunk-by-chunk slices reduced on the second stream
     const bool sliced = overlap_req && p->d.swizzle == GEMM_RS_SWIZZLE_IDENTITY && p->aux;
+    // one launch: each tile's last producer sums it
+    const bool last_arriver = (run_flags & GEMM_RS_LAST_ARRIVER) && do_gemm && do_reduce &&
+                              !p->d.materialize_sub && p->d.dtype == GEMM_RS_BF16 &&
+                              fused_reduce_supported(p->g.BM, p->g.BN, p->g.W);
     hipError_t e = hipSuccess;
+    if (last_arriver) {
+        GemmArgs x = a;
+        x.fuse_reduce = kFuseLastArriver;
+        x.release_flags = 1;
+        x.counters = p->counters;
+        x.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
+        x.groups = p->d.groups;
+        x.out = out;
+        x.err = p->err;
+        e = launch_gemm_bf16(x, s);
+        return e == hipSuccess ? GEMM_RS_OK : GEMM_RS_ERR_HIP;
+    }
     if (fused) {
         // Every rank visits its own chunk last, so rank d's last n = T/W
         // tiles (the tiles of chunk d) are the last contribution to each of
@@ -318,7 +336,7 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
             GemmArgs x = a;
             x.b_offset = W * k0;
             x.n_blocks = W * (T - k0);
-            x.fuse_reduce = 1;
+            x.fuse_reduce = kFuseOwner;
             x.groups = p->d.groups;
             x.out = out;
             x.err = p->err;
@@ -496,7 +514,7 @@ int gemm_rs_run_noalloc(const gemm_rs_desc_t *desc, const void *A, const void *B
                         const void *C, float alpha, float beta, void *out, void *stream,
                         uint32_t run_flags, int32_t *status) {
     if (!desc) return GEMM_RS_ERR_INVALID_ARG;
-    const uint32_t allowed = GEMM_RS_RUN_ALL | GEMM_RS_OVERLAP_REDUCE;
+    const uint32_t allowed = GEMM_RS_RUN_ALL | GEMM_RS_OVERLAP_REDUCE | GEMM_RS_LAST_ARRIVER;
     if ((run_flags & GEMM_RS_RUN_ALL) != GEMM_RS_RUN_ALL || (run_flags & ~allowed))
         return GEMM_RS_ERR_INVALID_ARG;
     if (status && ((uintptr_t)status & 15u)) return GEMM_RS_ERR_INVALID_ARG;

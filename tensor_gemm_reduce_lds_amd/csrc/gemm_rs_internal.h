@@ -162,17 +162,14 @@ __device__ inline void record_error(int32_t *err, int code, int32_t r, int32_t t
 }
 
 // Bounded wait until *f == 1 (0 = idle, 1 = ready, anything else breaks the
-// protocol).  With `acquire` the load is an agent-scope acquire (producers
-// may still be running); without it a relaxed load (producers finished in
-// an earlier launch on the stream).  Returns 0, or the error code after
-// recording it.
+// protocol), with relaxed agent-scope loads: every waiter here runs after its
+// producers' launch on the stream, whose boundary makes their stores
+// visible.  Returns 0, or the error code after recording it.
 __device__ inline int wait_flag_set(uint32_t *f, uint64_t timeout_ticks, int32_t *err,
-                                    int32_t r, int32_t t, bool acquire) {
+                                    int32_t r, int32_t t) {
     const uint64_t t0 = wall_clock64();
     for (;;) {
-        const uint32_t v =
-            acquire ? __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
-                    : __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (v == 1u) return 0;
         if (v != 0u) {
             record_error(err, GEMM_RS_ERR_PROTOCOL, r, t, v);
@@ -186,6 +183,8 @@ __device__ inline int wait_flag_set(uint32_t *f, uint64_t timeout_ticks, int32_t
     }
 }
 
+enum { kFuseNone = 0, kFuseOwner = 1, kFuseLastArriver = 2 };
+
 struct GemmArgs {
     TileGeom g;
     const void *A;       // [W][M][K]
@@ -198,7 +197,7 @@ struct GemmArgs {
     int32_t staging_bf16;   // 1: stage partials as bfloat16 (round to nearest even)
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
-    int32_t release_flags;  // 1: agent-scope release (concurrent consumer)
+    int32_t release_flags;  // 1: agent-scope release before the flag (consumer in this launch)
     uint32_t b_offset;      // first logical block of this launch (launch slices)
     uint32_t n_blocks;      // workgroups in this launch
     int32_t xcd_rank_major; // 1: logical_block's XCD map, 0: block = b_offset + blockIdx.x
@@ -211,12 +210,18 @@ struct GemmArgs {
     uint32_t epoch;
     uint64_t timeout_ticks;
     int32_t *err;
-    // owner-fused reduce (remote-first order, the launch of every rank's
-    // own-chunk tiles): workgroup (rank r, tile t) is the last contribution
-    // to tile t; it checks and resets the other ranks' flags for t, sums
-    // the tile's W partials (the others from their staging slots, its own
-    // from registers) in the reduce order and writes `out` (bf16)
+    // reduce fused into the GEMM (kFuseOwner or kFuseLastArriver; 0 = none).
+    // kFuseOwner (remote-first order, the launch of every rank's own-chunk
+    // tiles): workgroup (rank r, tile t) is the last contribution to tile
+    // t; it checks and resets the other ranks' flags for t, sums the
+    // tile's W partials (the others from their staging slots, its own from
+    // registers) in the reduce order and writes `out` (bf16).
+    // kFuseLastArriver (one launch, any order): every producer stages its
+    // partial, releases its flag and counts itself in on counters[t]; the
+    // W-th sums the tile the same way.
     int32_t fuse_reduce;
+    uint32_t *counters;     // [T] producer count per tile (kFuseLastArriver)
+    int32_t keep_flags;     // kFuseLastArriver: leave the flags at 1
     int32_t groups;         // reduce order: G groups of W/G ranks (1: flat)
     void *out;              // [M][N]
 };
@@ -227,7 +232,6 @@ struct ReduceArgs {
     TileGeom g;
     int32_t order, groups;   // groups == 1 for flat
     int32_t keep_flags;
-    int32_t acquire;         // 1: producers may run concurrently
     int32_t units_per_tile;  // BM / kReduceRows
     uint64_t timeout_ticks;  // device wall-clock ticks
     const void *staging;     // float, or bfloat16 bits (staging_bf16)

@@ -1,8 +1,9 @@
 // Flag-gated, fixed-order W-way reduction of the staging slots.
 //
 // Work unit: up to kReduceRows rows of one tile.  A unit first waits until
-// every rank's flag for its tile reads 1 (agent-scope acquire, bounded by a
-// timeout on the constant-rate device clock), then sums the W fp32 slots of
+// every rank's flag for its tile reads 1 (bounded by a timeout on the
+// constant-rate device clock; the producers ran in an earlier launch on the
+// stream), then sums the W fp32 slots of
 // each element in a fixed order and writes the rank's chunk rows of `out`.
 // The last unit of a tile to pass the wait puts the tile's flags back to 0,
 // so no buffer is ever cleared between runs (page "flux实现：sm80 gemm+rs",
@@ -22,27 +23,17 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Threads [0, count) each wait on one flag; true if all ready.  With
-// `acquire` (producers may still be running) the waits are agent-scope
-// acquires and every thread then takes an acquire fence, so loads issued
-// afterwards see what the producers stored before releasing.  Without it
-// (producers finished in an earlier kernel on the stream) the stream
-// order already makes their stores visible and plain loads suffice.
+// Threads [0, count) each wait on one flag; true if all ready.  The
+// producers finished in an earlier launch on the stream, whose boundary
+// already makes their stores visible, so relaxed loads suffice.
 __device__ bool wait_flags(uint32_t *base, int64_t stride, int count,
                            uint64_t timeout_ticks, int32_t *err, int32_t rank0,
-                           int32_t tile, bool acquire) {
-    __shared__ int failed;
-    if (threadIdx.x == 0) failed = 0;
-    __syncthreads();
+                           int32_t tile) {
+    int failed = 0;
     const int i = threadIdx.x;
-    if (i < count) {
-        if (wait_flag_set(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile,
-                          acquire))
-            atomicOr(&failed, 1);
-    }
-    __syncthreads();
-    if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return failed == 0;
+    if (i < count)
+        failed = wait_flag_set(base + (int64_t)i * stride, timeout_ticks, err, rank0 + i, tile);
+    return !__syncthreads_or(failed);
 }
 
 __device__ __forceinline__ void store_out4(void *out, int64_t idx, f32x4_t y, bool bf16) {
@@ -182,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     unit_tile(a, &t, &slab);
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
-    if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t, a.acquire)) return;
+    if (!wait_flags(a.flags + t, g.T, g.W, a.timeout_ticks, a.err, 0, t)) return;
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(&a.counters[t], 1u);
         if (old == (uint32_t)U - 1) {   // every unit of the tile has passed
@@ -243,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.flags + (int64_t)grp * L * g.T + t, g.T, L,
-                    a.timeout_ticks, a.err, grp * L, t, a.acquire))
+                    a.timeout_ticks, a.err, grp * L, t))
         return;
     if (threadIdx.x == 0) {
         uint32_t *cnt = &a.counters[(int64_t)grp * g.T + t];
@@ -271,11 +262,13 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
         float *dst = a.sub + ((d * G + grp) * g.Mc + il) * g.N + col;
         __builtin_nontemporal_store(s, (f32x4_t *)dst);
     }
-    __threadfence();
+    // the consumer (the final stage) runs in the next launch on the stream,
+    // whose boundary makes these stores visible: the sub-flag is a plain
+    // store after the workgroup's stores
     __syncthreads();
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.sub_flags[(int64_t)grp * per_group + unit], 1u,
-                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Materialised two-level, stage 2: y = ((S_0 + S_1) + ...) -> out.
@@ -289,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void reduce_final_sub_kernel(ReduceArgs a
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
 
     if (!wait_flags(a.sub_flags + unit, per_group, G, a.timeout_ticks,
-                    a.err, 0, t, a.acquire))
+                    a.err, 0, t))
         return;
     // a sub-flag has exactly one consumer: reset it right after the wait
     if (threadIdx.x < G && !a.keep_flags)

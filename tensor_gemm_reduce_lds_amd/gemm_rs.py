@@ -31,6 +31,7 @@ ORDER_FLAT, ORDER_TWO_LEVEL = 0, 1
 SWIZZLE_REMOTE_FIRST, SWIZZLE_SELF_FIRST, SWIZZLE_IDENTITY, SWIZZLE_TILE_INTERLEAVED = 0, 1, 2, 3
 STAGING_F32, STAGING_BF16 = 0, 1
 RUN_GEMM, RUN_REDUCE, KEEP_FLAGS, TRACE_TILES, OVERLAP_REDUCE = 1, 2, 4, 8, 16
+LAST_ARRIVER = 32
 RUN_ALL = RUN_GEMM | RUN_REDUCE
 AG_RUN_COPY, AG_RUN_GEMM, AG_FUSED, AG_EXPECT_NEXT = 1, 2, 4, 8
 AG_RUN_ALL = AG_RUN_COPY | AG_RUN_GEMM

@@ -133,7 +133,7 @@ def make_inputs(w: Workload, seed: int = 0, dist: Optional[str] = None,
     dist = dist or w.dist
     A = np.empty((w.W, w.M, w.K), dtype=np.float32)
     B = np.empty((w.W, w.K, w.N), dtype=np.float32)
-    b_scale = 1.0 / np.sqrt(w.K) if dist == "normal" else 1.0
+    b_scale = 1.0 / np.sqrt(w.K) if dist == "normal" and w.K > 0 else 1.0
     for r in range(w.W):
         A[r] = _draw(_rng(seed, w.index, KIND_A, r), (w.M, w.K), dist, 1.0)
         B[r] = _draw(_rng(seed, w.index, KIND_B, r), (w.K, w.N), dist, b_scale)

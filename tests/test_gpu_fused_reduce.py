@@ -251,3 +251,118 @@ def test_ineligible_configurations_take_the_serial_path():
                 assert flags(plan).all()
             else:
                 assert not flags(plan).any()
+
+
+# ------------------------------------------------------ last-arriver reduce
+LAST = G.RUN_ALL | G.LAST_ARRIVER
+
+
+def _serial_and_last(w, x, over, rounds=2, poison=False):
+    """Serial bits, then `rounds` last-arriver passes (staging filled with
+    NaN before the first: a summing workgroup that read a partial before
+    its producer's release would put NaN into the output)."""
+    dev = to_device(x, w)
+    with G.Plan(**desc_fields(w, **over)) as plan:
+        ref = new_out(w)
+        run_checked(plan, dev, w, ref)
+        if poison:
+            hip().hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+            assert hip().hipMemset(plan.info.staging, 0xFF, plan.info.staging_bytes) == 0
+        got = new_out(w)
+        for _ in range(rounds):
+            run_checked(plan, dev, w, got, LAST)
+            assert not flags(plan).any()
+        return out_bits(ref), out_bits(got), out_to_f64(got, w)
+
+
+@pytest.mark.parametrize("swizzle", [G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_IDENTITY,
+                                     G.SWIZZLE_TILE_INTERLEAVED])
+@pytest.mark.parametrize("name,w,over", SMALL, ids=[c[0] for c in SMALL])
+def test_last_arriver_small_full_parity(name, w, over, swizzle):
+    """Any tile order: every tile is summed once, by whichever of its W
+    producers counts in last, bit for bit as the serial reduce sums it."""
+    x = I.make_inputs(w)
+    say("last arriver small", name, swizzle)
+    serial, got_bits, got = _serial_and_last(w, x, dict(over, swizzle=swizzle), poison=True)
+    assert np.array_equal(got_bits, serial)
+    kw = oracle_kw(w)
+    ref = O.reference_rows(x["A"], x["B"], x["C"], **kw)
+    if over.get("staging_dtype") == G.STAGING_BF16:
+        mag = sum(np.abs(O.partial_rows(x["A"], x["B"], x["C"], dtype=kw["dtype"],
+                                        alpha=w.alpha, beta=w.beta, ldc=w.ldc, r=r))
+                  for r in range(w.W))
+        check_bf16_staging(got, ref, mag)
+    else:
+        check_tolerance(got, ref, w.dtype)
+
+
+@pytest.mark.parametrize("name", ["straddle_2lvl", "full_c", "bf16_staging_straddle"])
+def test_last_arriver_small_integer_exact(name):
+    w, over = {c[0]: (c[1], c[2]) for c in SMALL}[name]
+    if over.get("staging_dtype") == G.STAGING_BF16:
+        w = I.with_shape(w, K=512)
+    x = I.make_inputs(w, dist="ternary", c_dist="ternary")
+    say("last arriver integer", name)
+    serial, got, _ = _serial_and_last(w, x, over)
+    em = O.emulate_rows(x["A"], x["B"], x["C"], **oracle_kw(w),
+                        staging_dtype=over.get("staging_dtype", O.STAGING_F32))
+    assert np.array_equal(got, em.view(got.dtype))
+    assert np.array_equal(serial, got)
+
+
+@pytest.mark.parametrize("name", ["llama70b", "ragged_2lvl"])
+def test_last_arriver_full_size_sampled_parity(name):
+    """Full size, staging poisoned with NaN first: the output has no NaN,
+    equals the serial bits everywhere and the oracle on sampled rows and
+    elements."""
+    w = W70[name]
+    rng = np.random.default_rng(41)
+    x = I.make_inputs(w)
+    say("last arriver full", name)
+    serial, got_bits, got = _serial_and_last(w, x, {}, rounds=1, poison=True)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got_bits, serial)
+    kw = oracle_kw(w)
+    rows = _sample_rows(w, rng)
+    ref_rows = np.concatenate([O.reference_rows(x["A"], x["B"], x["C"], row_lo=i,
+                                                row_hi=i + 1, **kw) for i in rows])
+    check_tolerance(got[rows], ref_rows, w.dtype)
+    ii = rng.integers(0, w.M, size=3000)
+    jj = rng.integers(0, w.N, size=3000)
+    ref_e = O.reference_elems(x["A"], x["B"], x["C"], ii=ii, jj=jj, **kw)
+    check_tolerance(got[ii, jj], ref_e, w.dtype)
+
+
+def test_last_arriver_flag_life_cycle_and_mixed_runs():
+    """KEEP_FLAGS leaves every flag at 1 (the counters still reset); the
+    next serial GEMM re-sets them and its reduce clears them; last-arriver,
+    owner-fused and serial passes alternate on one stream without a host
+    sync and give the same bits; a combined OVERLAP_REDUCE | LAST_ARRIVER
+    is refused."""
+    import torch
+    w = dict((c[0], c[1]) for c in SMALL)["straddle_2lvl"]
+    x = I.make_inputs(w)
+    dev = to_device(x, w)
+    say("last arriver life cycle")
+    with G.Plan(**desc_fields(w)) as plan:
+        ref = new_out(w)
+        run_checked(plan, dev, w, ref)
+        o = new_out(w)
+        run_checked(plan, dev, w, o, LAST | G.KEEP_FLAGS)
+        assert flags(plan).all()
+        assert np.array_equal(out_bits(o), out_bits(ref))
+        run_checked(plan, dev, w, o)
+        assert not flags(plan).any()
+        s = torch.cuda.current_stream()
+        outs = [new_out(w) for _ in range(6)]
+        for k, oo in enumerate(outs):
+            plan.run(dev["A"], dev["B"], dev["C"], w.alpha, w.beta, oo, s,
+                     (LAST, FUSED, G.RUN_ALL)[k % 3])
+        rc, detail = plan.status(s)
+        assert rc == G.OK, detail
+        for oo in outs:
+            assert np.array_equal(out_bits(oo), out_bits(ref))
+        assert not flags(plan).any()
+        rc = G.gemm_rs_run(plan.handle, dev["A"], dev["B"], dev["C"], w.alpha, w.beta, o, s,
+                           LAST | G.OVERLAP_REDUCE)
+        assert rc == G.ERR_INVALID_ARG
