@@ -127,9 +127,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 
     const TileGeom &g = a.g;
     int32_t r, t;
-    const uint32_t b = a.xcd_rank_major ? logical_block(g, a.b_offset, a.n_blocks, blockIdx.x)
-                                        : a.b_offset + blockIdx.x;
-    tile_of_block(g, b, &r, &t);
+    uint32_t b;
+    if (a.slot_tab) {
+        // the full launch: the slot's rank and tile were tabulated with the
+        // plan (one scalar load instead of the tile-order arithmetic, which
+        // every wave of the workgroup would repeat on the shared scalar unit)
+        const uint32_t v = a.slot_tab[blockIdx.x];
+        r = (int32_t)(v >> kSlotTileBits);
+        t = (int32_t)(v & ((1u << kSlotTileBits) - 1u));
+        b = a.trace ? logical_block(g, 0, a.n_blocks, blockIdx.x) : 0u;   // trace index only
+    } else {
+        b = a.xcd_rank_major ? logical_block(g, a.b_offset, a.n_blocks, blockIdx.x)
+                             : a.b_offset + blockIdx.x;
+        tile_of_block(g, b, &r, &t);
+    }
     const int32_t tm = t / g.tiles_n, tn = t - (t / g.tiles_n) * g.tiles_n;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -285,6 +296,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < KT) issue(s, s);
+    // the bias row of the tile's columns (ldc == 0): one 8-byte load per
+    // lane, issued with the first operand loads, so it has arrived by the
+    // epilogue
+    uint2 cb_row = {0u, 0u};
+    if (a.has_c && a.ldc == 0)
+        cb_row = *(const uint2 *)((const uint16_t *)a.C + col0 + (lane % (BN / 4)) * 4);
     if constexpr (FW > 0) if (a.fuse_reduce == kFuseOwner) {
         // owner-fused reduce: every other rank's partial of this tile was
         // staged by an earlier launch on the stream (so it is visible
@@ -355,11 +372,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // in order), so no load sits between two stores.
     auto epilogue = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
-        uint2 cb_row = {0u, 0u};
         float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // the bias row's 4 columns, widened
         if constexpr (MODE == 1) {
-            cb_row = *(const uint2 *)(Cp + col0 + scol);
-            asm volatile("" : "+v"(cb_row.x), "+v"(cb_row.y));   // wait here, once
             cf[0] = __uint_as_float(cb_row.x << 16);
             cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
             cf[2] = __uint_as_float(cb_row.y << 16);
@@ -523,8 +537,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         const int q_lo = r;                          // remote j < r is rank j, else j+1
         float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (MODE == 1) {
-            uint2 cb_row = *(const uint2 *)(Cp + col0 + scol);
-            asm volatile("" : "+v"(cb_row.x), "+v"(cb_row.y));
             cf[0] = __uint_as_float(cb_row.x << 16);
             cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
             cf[2] = __uint_as_float(cb_row.y << 16);

@@ -35,6 +35,7 @@ struct gemm_rs_plan_s {
     uint32_t *sub_flags;     // [G][T*units]
     int32_t *err;            // 4 words
     int32_t *trace;          // [W*T]
+    uint32_t *slot_tab;      // [W*T] (rank, tile) of each slot of the full launch, or null
     int64_t staging_bytes, flags_bytes, counters_bytes, sub_bytes,
         sub_flags_bytes, trace_bytes;
     // overlapped reduce: an auxiliary stream (default priority) and events
@@ -137,6 +138,7 @@ void free_plan(gemm_rs_plan_s *p) {
     (void)hipFree(p->sub_flags);
     (void)hipFree(p->err);
     (void)hipFree(p->trace);
+    (void)hipFree(p->slot_tab);
     for (int i = 0; i < kEvents; ++i)
         if (p->slice_done[i]) (void)hipEventDestroy(p->slice_done[i]);
     if (p->aux_done) (void)hipEventDestroy(p->aux_done);
@@ -274,6 +276,8 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
         GemmArgs x = a;
         x.b_offset = b_lo;
         x.n_blocks = b_hi - b_lo;
+        // the tabulated slots hold the full launch only
+        x.slot_tab = (b_lo == 0 && b_hi == a.n_blocks) ? p->slot_tab : nullptr;
         if (x.n_blocks == 0) return hipSuccess;
         return p->d.dtype == GEMM_RS_BF16 ? launch_gemm_bf16(x, st) : launch_gemm_f32(x, st);
     };
@@ -311,6 +315,7 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
     hipError_t e = hipSuccess;
     if (last_arriver) {
         GemmArgs x = a;
+        x.slot_tab = p->slot_tab;   // the full launch
         x.fuse_reduce = kFuseLastArriver;
         x.release_flags = 1;
         x.counters = p->counters;
@@ -449,6 +454,9 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     if (e == hipSuccess) e = hipMalloc(&p->counters, p->counters_bytes);
     if (e == hipSuccess) e = hipMalloc(&p->err, 4 * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc(&p->trace, p->trace_bytes);
+    // the slot table packs the tile id in 26 bits; larger grids derive it
+    if (e == hipSuccess && p->g.T < (1 << kSlotTileBits))
+        e = hipMalloc(&p->slot_tab, p->trace_bytes);
     if (e == hipSuccess && d.materialize_sub) {
         e = hipMalloc(&p->sub, p->sub_bytes);
         if (e == hipSuccess) e = hipMalloc(&p->sub_flags, p->sub_flags_bytes);
@@ -464,6 +472,7 @@ int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out) {
     // for (unrelated work on the device is not)
     if (e == hipSuccess) e = clear_protocol_state(p, p->aux);
     if (e == hipSuccess) e = hipMemsetAsync(p->trace, 0xff, p->trace_bytes, p->aux);
+    if (e == hipSuccess && p->slot_tab) e = launch_slot_table(p->g, p->slot_tab, p->aux);
     if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
     if (e != hipSuccess) {
         free_plan(p);

@@ -198,6 +198,10 @@ struct GemmArgs {
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
     int32_t release_flags;  // 1: agent-scope release before the flag (consumer in this launch)
+    // (rank << 26) | tile of every slot of the full launch (b_offset 0,
+    // n_blocks W*T, the XCD map), tabulated once per plan; null: derive it
+    // with logical_block and tile_of_block (launch slices, no plan)
+    const uint32_t *slot_tab;
     uint32_t b_offset;      // first logical block of this launch (launch slices)
     uint32_t n_blocks;      // workgroups in this launch
     int32_t xcd_rank_major; // 1: logical_block's XCD map, 0: block = b_offset + blockIdx.x
@@ -259,6 +263,9 @@ hipError_t launch_reduce(const ReduceArgs &a, int dtype, hipStream_t s);
 hipError_t launch_reduce_sub(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_reduce_final_sub(const ReduceArgs &a, int dtype, hipStream_t s);
 hipError_t launch_tile_order(const TileGeom &g, int32_t *trace, hipStream_t s);
+// Fill tab[h] = (rank << 26) | tile for the W*T slots of the full launch.
+hipError_t launch_slot_table(const TileGeom &g, uint32_t *tab, hipStream_t s);
+constexpr int kSlotTileBits = 26;
 hipError_t launch_clear_words(uint32_t *a, int64_t na, uint32_t *b, int64_t nb,
                               hipStream_t s);
 

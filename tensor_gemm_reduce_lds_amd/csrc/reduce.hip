@@ -312,6 +312,15 @@ __global__ void clear_words_kernel(uint32_t *a, int64_t na, uint32_t *b, int64_t
     else if (i < na + nb) b[i - na] = 0u;
 }
 
+__global__ void slot_table_kernel(TileGeom g, uint32_t *tab) {
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t n = (uint32_t)g.W * (uint32_t)g.T;
+    if (h >= n) return;
+    int32_t r, t;
+    tile_of_block(g, logical_block(g, 0, n, (uint32_t)h), &r, &t);
+    tab[h] = ((uint32_t)r << kSlotTileBits) | (uint32_t)t;
+}
+
 __global__ void tile_order_kernel(TileGeom g, int32_t *trace) {
     const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= (int64_t)g.W * g.T) return;
@@ -397,6 +406,13 @@ hipError_t launch_clear_words(uint32_t *a, int64_t na, uint32_t *b, int64_t nb,
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        a, na, b, nb);
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_table(const TileGeom &g, uint32_t *tab, hipStream_t s) {
+    const int64_t n = (int64_t)g.W * g.T;
+    hipLaunchKernelGGL(slot_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       g, tab);
     return hipGetLastError();
 }
 
