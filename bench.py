@@ -327,6 +327,9 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the overlapped-reduce timing (profiling runs: every "
                          "GEMM and reduce launch is then a full launch)")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="time only the owner-fused steps (the reduce fused into the last "
+                         "tile-order step) and print their object (profiling runs of that mode)")
     ap.add_argument("--ag-only", action="store_true",
                     help="time only the all-gather + GEMM half and print its object "
                          "(profiling runs of that path)")
@@ -382,6 +385,33 @@ def main():
         torch.cuda.synchronize()
         log("bench: calibration copy of %d MiB done" % args.copy_calibration)
         del src, dst
+
+    if args.fused_only:
+        # warm-up, then the timed owner-fused steps with HIP events around
+        # each (one run call: both GEMM launches)
+        for _ in range(args.warmup):
+            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            fev[k][0].record(stream)
+            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_ALL | G.OVERLAP_REDUCE)
+            fev[k][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        rc, detail = plan.status(stream)
+        if rc != G.OK:
+            raise RuntimeError("fused run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+        ms = sum(e[0].elapsed_time(e[1]) for e in fev) / args.steps
+        print(json.dumps({"fused": {"workload": w.name, "steps": args.steps,
+                                    "ms_per_step": round(wall * 1e3 / args.steps, 4),
+                                    "ms_per_step_events": round(ms, 4),
+                                    "value": round(w.flops / (ms * 1e-3) / 1e12, 2)}}),
+              flush=True)
+        plan.close()
+        return
 
     def step(ev=None):
         if ev is not None:

@@ -310,11 +310,15 @@ int gemm_ag_run(gemm_ag_plan_t p, const void *X, const void *B, void *out, void 
     hipError_t e = hipSuccess;
     if (do_copy && do_gemm && (run_flags & GEMM_AG_FUSED)) {
         // the copies start once earlier work on `stream` (which wrote X) is
-        // done, on the second stream, while the GEMM's tiles wait for them
+        // done, on the second stream, while the GEMM's tiles wait for them.
+        // The copy kernel is enqueued first: it waits for nothing, so its
+        // workgroups take their places before the gated GEMM's fill the
+        // CUs, and progress does not rest on the copies finding room beside
+        // waiting GEMM workgroups (which the register budget also leaves).
         e = hipEventRecord(p->ready, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(p->copy, p->ready, 0);
-        if (e == hipSuccess) e = launch_gemm_bf16(a, s);
         if (e == hipSuccess) e = launch_ag_copy(c, p->copy);
+        if (e == hipSuccess) e = launch_gemm_bf16(a, s);
         if (e == hipSuccess) e = hipEventRecord(p->copied, p->copy);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, p->copied, 0);
     } else {

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // Transposed 32x32 accumulator layout: lane holds output row (lane & 31)
     // of the block; registers 4q..4q+3 hold its columns 8q + 4*(lane/32)
     // + 0..3.
-    constexpr int EP_PITCH = BN * 4 + 16;          // bytes per staged row (padded)
+    constexpr int EP_PITCH = BN * 4 + 16;          // bytes per staged row (padded; fused epilogue)
     constexpr int LPR = BN / 4;                    // lanes per row (16 bytes each)
     constexpr int RPI = 64 / LPR;                  // rows per store instruction
     constexpr int SROWS = WGM * 32;                // rows per stripe
@@ -360,6 +360,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     static_assert(SROWS * EP_PITCH <= STAGES * STAGE, "stripe fits in the stage buffers");
     static_assert(ST_PER_WAVE * NW * RPI == SROWS, "stripe rows split evenly");
     static_assert(32 % (ST_PER_WAVE * RPI) == 0, "a wave's stripe rows stay in one 32-row group");
+    // The plain epilogue's stripes alternate between the two stages, with
+    // rows of BN*4 bytes whose 16-byte chunk c of row rr sits at c ^ (rr %
+    // 16): the 16 rows one write covers and the chunks one read covers both
+    // land on distinct banks without padding, so a stripe fits one stage.
+    // The stage that held step KT-2 is free on arrival (every wave has
+    // passed the barrier that followed its last reads of it), so the first
+    // stripe needs no barrier before it; the stage of step KT-1 is free
+    // once every wave has passed the first stripe's barrier.
+    constexpr int EP_ROW = BN * 4;
+    static_assert(SROWS * EP_ROW <= STAGE, "a stripe fits one stage");
+    static_assert(STAGES == 2, "stripes alternate between the two stages");
+    lds_char *const ep_buf[2] = {smem + (KT & 1) * STAGE, smem + ((KT + 1) & 1) * STAGE};
     const uint16_t *Cp = (const uint16_t *)a.C;
     const float alpha = a.alpha, beta = a.beta;
     const int h4 = 4 * (lane >> 5);
@@ -379,12 +391,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             cf[2] = __uint_as_float(cb_row.y << 16);
             cf[3] = __uint_as_float(cb_row.y & 0xffff0000u);
         }
-        __syncthreads();                            // every wave is done with the stages
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            // stage block i of every wave: stripe wm holds tile rows
-            // wm*WM + i*32 .. +31 across all BN columns
-            lds_char *stripe = smem + wm * 32 * EP_PITCH;
+            // stage block i of every wave: stripe rows wm*32 .. +31 hold tile
+            // rows wm*WM + i*32 .. +31 across all BN columns
+            lds_char *const buf = ep_buf[i & 1];
+            // stripe row sr, columns 4c .. 4c+3
+            auto at = [&](int sr, int c) __attribute__((always_inline)) {
+                return (__attribute__((address_space(3))) f32x4_t *)(
+                    buf + sr * EP_ROW + ((c ^ (sr & 15)) << 4));
+            };
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -392,8 +408,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                     f32x4_t x;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
-                    *(__attribute__((address_space(3))) f32x4_t *)(
-                        stripe + (lane & 31) * EP_PITCH + (wn * WN + j * 32 + 8 * q + h4) * 4) = x;
+                    *at(wm * 32 + (lane & 31), (wn * WN + j * 32 + 8 * q + h4) >> 2) = x;
                 }
             uint2 cb_full[ST_PER_WAVE];
             if constexpr (MODE == 2) {
@@ -426,8 +441,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             for (int k = 0; k < ST_PER_WAVE; ++k) {
                 const int sr = sr0 + k * RPI;               // row in the stripe set
                 const int64_t row = rowF + k * RPI;
-                f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
-                    smem + sr * EP_PITCH + scol * 4);
+                f32x4_t x = *at(sr, scol >> 2);
                 if (row < g.M) {
                     int32_t d = dF;
                     int64_t off = offF + (int64_t)(k * RPI) * g.N;
@@ -482,8 +496,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         uint16_t *dst = (uint16_t *)a.staging + offF;
 #pragma unroll
                         for (int k = 0; k < ST_PER_WAVE; ++k, dst += step) {
-                            f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
-                                smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
+                            f32x4_t x = *at(sr0 + k * RPI, scol >> 2);
                             if (add_c)
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
@@ -500,8 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         float *dst = (float *)a.staging + offF;
 #pragma unroll
                         for (int k = 0; k < ST_PER_WAVE; ++k, dst += step) {
-                            f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
-                                smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
+                            f32x4_t x = *at(sr0 + k * RPI, scol >> 2);
                             if (add_c)
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
@@ -514,7 +526,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             } else {
                 store_rows();
             }
-            if (i + 1 < FM) lds_barrier();          // the stripe buffer is reused
+            // no barrier here: the next stripe goes to the other stage, and
+            // the one after it waits for the next stripe's barrier, which
+            // every wave reaches after its reads of this one
         }
     };
     // ---- owner-fused reduce epilogue ----
