@@ -148,8 +148,12 @@ typedef struct gemm_rs_plan_s *gemm_rs_plan_t;
 /*
  * Introspection record (tests and benchmark).  Workspace pointers are
  * device addresses owned by the plan.
- *   staging      S[d][r][Mc][N] (float32, or bfloat16 bits with
- *                GEMM_RS_STAGING_BF16), slot (d,r) at element ((d*W + r)*Mc)*N
+ *   staging      W*W slots S[d][r] of slot_elems elements (float32, or
+ *                bfloat16 bits with GEMM_RS_STAGING_BF16): slot (d,r) at
+ *                element (d*W + r)*slot_elems holds [Mc][N] row-major;
+ *                slot_elems = Mc*N, rounded up to a multiple of 512 KiB
+ *                when a slot holds 8 MiB or more (the rest of the slot is
+ *                never read or written)
  *   flags        uint32 flag[r][t], r < W, t < T (t = tm*tiles_n + tn)
  *   sub          float32 sub[d][g][Mc][N] (materialize_sub only, else NULL)
  *   sub_flags    uint32 subflag[g][t] (materialize_sub only, else NULL)
@@ -167,11 +171,12 @@ typedef struct gemm_rs_info {
     void *sub_flags;
     void *trace;
     int64_t staging_bytes, flags_bytes, sub_bytes, sub_flags_bytes;
+    int64_t slot_elems;
 } gemm_rs_info_t;
 
 /*
  * gemm_rs_plan: validate *desc, choose defaults, allocate the workspace on
- * the current HIP device (staging W*M*N*4 bytes, flags, counters, error
+ * the current HIP device (staging W*W*slot_elems elements, flags, counters, error
  * word, trace, optional sub-group buffers) and zero the flags once,
  * synchronously.  On success *out owns all of it until gemm_rs_destroy.
  * Returns OK, INVALID_ARG (NULL desc/out, W outside 1..64, M or N < 1,
@@ -266,8 +271,9 @@ GEMM_RS_API int gemm_rs_run(gemm_rs_plan_t plan, const void *A, const void *B,
  *        asynchronous error (TIMEOUT or PROTOCOL) of the pass
  * Returns OK, INVALID_ARG / UNSUPPORTED (as gemm_rs_plan; materialize_sub
  * is UNSUPPORTED here), SCRATCH when the workspace (256 bytes + W*T*4 +
- * T*4, each rounded up to 256, + W*M*N*4 staging bytes, *2 with bfloat16
- * staging) exceeds 64 MiB, or HIP.  Every call on one GPU shares the same
+ * T*4, each rounded up to 256, + W*W*slot_elems staging elements of 4
+ * bytes, 2 with bfloat16 staging; see gemm_rs_info_t) exceeds 64 MiB, or
+ * HIP.  Every call on one GPU shares the same
  * array: calls that overlap on one GPU (two streams, or two threads) race
  * and give undefined results; calls ordered on one stream are safe.
  */

@@ -12,6 +12,9 @@ Contents
                      valid but unsupported).
 * ``Geometry``       the tile -> chunk map and the per-rank tile order
                      (swizzle), plus staging offsets and flag predictions.
+* ``staging_slot_elems``  the library's staging slot size (a restated
+                     layout rule, like the UNSUPPORTED limits in
+                     ``validate``).
 * ``reference_*``    the fp64 result (parity target), in C.
 * ``emulate_*``      a float pipeline emulation, bit-exact only where the
                      per-rank epilogue values are exact in float.
@@ -123,6 +126,21 @@ def validate(M, N, K, W, dtype, tile_m, tile_n, group_m=1, order=FLAT,
 # --------------------------------------------------------------------------
 # tile -> chunk map and swizzle
 # --------------------------------------------------------------------------
+def staging_slot_elems(Mc: int, N: int, elem_bytes: int) -> int:
+    """Elements from one staging slot to the next.
+
+    The library's staging layout, restated here so the tests can find a
+    slot (not a rule of the pages, which leave the buffer layout open): a
+    slot holds Mc x N partials, and once it holds 8 MiB or more its size is
+    rounded up to a multiple of 512 KiB, the rest of it unused.
+    """
+    nbytes = Mc * N * elem_bytes
+    if nbytes < 8 << 20:
+        return Mc * N
+    align = 512 << 10
+    return -(-nbytes // align) * align // elem_bytes
+
+
 class Geometry:
     """Tile grid, chunk ownership and per-rank tile order.
 
@@ -135,7 +153,8 @@ class Geometry:
     """
 
     def __init__(self, M, N, K, W, tile_m, tile_n, group_m=1,
-                 swizzle=REMOTE_FIRST, order=FLAT, groups=1, interleave=1):
+                 swizzle=REMOTE_FIRST, order=FLAT, groups=1, interleave=1,
+                 staging_dtype=STAGING_F32):
         self.M, self.N, self.K, self.W = M, N, K, W
         self.BM, self.BN = tile_m, tile_n
         self.g = max(1, group_m)
@@ -143,6 +162,7 @@ class Geometry:
         self.q = max(1, interleave)
         self.order, self.groups = order, (groups if order == TWO_LEVEL else 1)
         self.Mc = M // W
+        self.slot = staging_slot_elems(self.Mc, N, 2 if staging_dtype == STAGING_BF16 else 4)
         self.tiles_m = -(-M // tile_m)
         self.tiles_n = N // tile_n
         self.T = self.tiles_m * self.tiles_n
@@ -171,12 +191,14 @@ class Geometry:
     def staging_offset(self, d: int, r: int, i: int, j: int) -> int:
         """Element offset of (row i, col j) from rank r in slot (d, r).
 
-        Staging is destination-major S[d][r][Mc][N]: slot (d, r) is the
-        piece of rank r's output that rank d receives (the per-destination
-        reduce-scatter buffer the epilogue writes into, page "flux实现：sm80
-        gemm+rs", section "cutlass自定义epilogue–sm80", the StoreD paragraph).
+        Staging is destination-major: slot (d, r) is the piece of rank r's
+        output that rank d receives (the per-destination reduce-scatter
+        buffer the epilogue writes into, page "flux实现：sm80 gemm+rs",
+        section "cutlass自定义epilogue–sm80", the StoreD paragraph), rows
+        [Mc][N] row-major from the slot's start; slots are ``self.slot``
+        elements apart (``staging_slot_elems``).
         """
-        return ((d * self.W + r) * self.Mc + (i - d * self.Mc)) * self.N + j
+        return (d * self.W + r) * self.slot + (i - d * self.Mc) * self.N + j
 
     def sub_offset(self, d: int, g: int, i: int, j: int) -> int:
         """Element offset of (row i, col j) of group g's partial sum in the

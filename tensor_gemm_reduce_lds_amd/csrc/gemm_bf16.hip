@@ -429,14 +429,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             // and advanced by RPI rows per store; only a row that crosses
             // into the next chunk recomputes it
             const int sr0 = wave * ST_PER_WAVE * RPI + srow;
+            const int64_t slot_d = (int64_t)g.W * g.slot, slot_r = (int64_t)r * g.slot;
             const int64_t rowF = row0 + (sr0 >> 5) * WM + i * 32 + (sr0 & 31);
             const int32_t dF = (int32_t)((uint64_t)rowF / (uint64_t)g.Mc);
             const int64_t next_chunk = (int64_t)(dF + 1) * g.Mc;
             const int64_t offF =
                 a.plain_out ? ((int64_t)r * g.M + rowF) * g.N + col0 + scol
-                            : (((int64_t)dF * g.W + r) * g.Mc + (rowF - (int64_t)dF * g.Mc)) * g.N +
+                            : (int64_t)dF * slot_d + slot_r + (rowF - (int64_t)dF * g.Mc) * g.N +
                                   col0 + scol;
-            auto store_rows = [&] {
+            auto store_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int k = 0; k < ST_PER_WAVE; ++k) {
                 const int sr = sr0 + k * RPI;               // row in the stripe set
@@ -449,8 +450,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                         d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
                         off = a.plain_out
                                   ? ((int64_t)r * g.M + row) * g.N + col0 + scol
-                                  : (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) *
-                                            g.N + col0 + scol;
+                                  : (int64_t)d * slot_d + slot_r + (row - (int64_t)d * g.Mc) * g.N +
+                                        col0 + scol;
                     }
                     if constexpr (MODE != 0) {
                         const uint2 cb = MODE == 1 ? cb_row : cb_full[k];
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         constexpr int NR = FW > 1 ? FW - 1 : 1;      // remote partials per element
         typedef typename std::conditional<SB, u32x2_t, f32x4_t>::type raw_t;
         const int L = FW / a.groups;                 // ranks per group
-        const int64_t slot = g.Mc * g.N;             // elements from slot (d,q) to (d,q+1)
+        const int64_t slot = g.slot;                 // elements from slot (d,q) to (d,q+1)
         const int q_lo = r;                          // remote j < r is rank j, else j+1
         float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (MODE == 1) {
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         }
         __syncthreads();                            // every wave is done with the stages
         // the remote partials of one row (wave-uniform row for BN = 256)
-        auto load_row = [&](int64_t base, raw_t (&v)[NR]) {
+        auto load_row = [&](int64_t base, raw_t (&v)[NR]) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
                 const int64_t idx = base + (int64_t)(j < q_lo ? j : j + 1) * slot;
@@ -597,12 +598,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             const int sr0 = wave * ST_PER_WAVE * RPI + srow;
             const int64_t rowF = row0 + (sr0 >> 5) * WM + i * 32 + (sr0 & 31);
             // row k of this lane: rowF + k*RPI; chunk and slot-0 offset per row
-            auto row_base = [&](int k, int32_t *d_out) -> int64_t {
+            auto row_base = [&](int k, int32_t *d_out) __attribute__((always_inline)) -> int64_t {
                 int64_t row = rowF + (int64_t)k * RPI;
                 if (row > g.M - 1) row = g.M - 1;   // ragged M: a valid row, not stored
                 const int32_t d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
                 *d_out = d;
-                return (((int64_t)d * FW) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N + col0 + scol;
+                return ((int64_t)d * FW) * g.slot + (row - (int64_t)d * g.Mc) * g.N + col0 + scol;
             };
             raw_t cur[NR], nxt[NR];
             int32_t d_cur, d_nxt = 0;

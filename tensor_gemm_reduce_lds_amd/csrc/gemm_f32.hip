@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         float x = a.alpha * acc[v];
         if (a.has_c && d == r) x += a.beta * Cp[row * a.ldc + col];
         float *dst = (float *)a.staging +
-                     (((int64_t)d * g.W + r) * g.Mc + (row - (int64_t)d * g.Mc)) * g.N;
+                     ((int64_t)d * g.W + r) * g.slot + (row - (int64_t)d * g.Mc) * g.N;
         __builtin_nontemporal_store(x, dst + col);
     }
 

@@ -201,8 +201,9 @@ int resolve(const gemm_rs_desc_t &desc, gemm_rs_plan_s *p) {
     while ((1 << g.bm_shift) < bm) ++g.bm_shift;
     p->units_per_tile = (bm + kReduceRows - 1) / kReduceRows;
 
-    p->staging_bytes =
-        (int64_t)d.W * d.M * d.N * (d.staging_dtype == GEMM_RS_STAGING_BF16 ? 2 : 4);
+    const int staging_elem = d.staging_dtype == GEMM_RS_STAGING_BF16 ? 2 : 4;
+    g.slot = staging_slot_elems(g.Mc, g.N, staging_elem);
+    p->staging_bytes = (int64_t)d.W * d.W * g.slot * staging_elem;
     p->flags_bytes = (int64_t)d.W * g.T * 4;
     p->counters_bytes = (int64_t)g.T * 4;
     p->trace_bytes = (int64_t)d.W * g.T * 4;
@@ -506,6 +507,7 @@ int gemm_rs_query(gemm_rs_plan_t p, gemm_rs_info_t *info) {
     info->flags_bytes = p->flags_bytes;
     info->sub_bytes = p->sub_bytes;
     info->sub_flags_bytes = p->sub_flags_bytes;
+    info->slot_elems = p->g.slot;
     info->workspace_bytes = p->staging_bytes + p->flags_bytes +
                             p->counters_bytes * (1 + (p->sub_counters ? p->d.groups : 0)) +
                             p->sub_bytes + p->sub_flags_bytes + p->trace_bytes + 16;

@@ -15,10 +15,24 @@ constexpr int kThreads = 256;
 // Geometry the kernels need to place tiles.
 struct TileGeom {
     int64_t M, N, K, Mc;
+    int64_t slot;        // staging elements from slot (d,r) to the next (>= Mc*N)
     int32_t W, BM, BN, tiles_m, tiles_n, T, group_m, swizzle;
     int32_t interleave;  // q >= 1: tiles per destination visit (tile-interleaved order)
     int32_t bm_shift;    // log2(BM)
 };
+
+// Staging slot size in elements: Mc*N, rounded up to a multiple of
+// 512 KiB once a slot holds 8 MiB or more.  A slot stride that is an odd
+// multiple of 256 KiB (1000 rows of 8192 fp32, for one) was measured to
+// cost the reduce's eight concurrent slot streams ~4% of their HBM rate;
+// at 512 KiB multiples they run at the rate of power-of-two strides.  The
+// rounding adds at most 1/16 to a slot.
+__host__ __device__ inline int64_t staging_slot_elems(int64_t Mc, int64_t N, int elem_bytes) {
+    const int64_t bytes = Mc * N * elem_bytes;
+    const int64_t align = (int64_t)512 << 10;
+    if (bytes < ((int64_t)8 << 20)) return Mc * N;
+    return (bytes + align - 1) / align * align / elem_bytes;
+}
 
 // All tile-order arithmetic is 32-bit: b < W*T < 2^31 and d*Mc < M < 2^31
 // (the plan rejects larger problems), and BM is a power of two.
@@ -193,7 +207,7 @@ struct GemmArgs {
     int64_t ldc;
     int32_t has_c;
     float alpha, beta;
-    void *staging;       // [W][W][Mc][N] float, or bfloat16 bits
+    void *staging;       // [W][W] slots of g.slot elements ([Mc][N] used), float or bfloat16 bits
     int32_t staging_bf16;   // 1: stage partials as bfloat16 (round to nearest even)
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null

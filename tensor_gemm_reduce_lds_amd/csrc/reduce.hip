@@ -193,11 +193,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     const int RPP = kThreads / C4;            // rows per pass
     const int c4 = threadIdx.x % C4;
     const int64_t col = (int64_t)tn * g.BN + c4 * 4;
-    const int64_t stride = g.Mc * g.N;
+    const int64_t stride = g.slot;
     if constexpr (!ROWS2) {
         for (int64_t row = lo + threadIdx.x / C4; row < hi; row += RPP) {
             const int64_t d = row / g.Mc;
-            const int64_t idx = ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
+            const int64_t idx = (d * W) * g.slot + (row - d * g.Mc) * g.N + col;
             store_out4(a.out, row * g.N + col, ordered_sum<WT, LT, SB>(a.staging, idx, stride, W, L),
                        OUT_BF16);
         }
@@ -207,10 +207,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     for (int64_t row = lo + threadIdx.x / C4; row < hi; row += 2 * RPP) {
         const int64_t row2 = row + RPP;
         const int64_t d = row / g.Mc;
-        const int64_t idx = ((d * W) * g.Mc + (row - d * g.Mc)) * g.N + col;
+        const int64_t idx = (d * W) * g.slot + (row - d * g.Mc) * g.N + col;
         if (row2 < hi) {
             const int64_t d2 = row2 / g.Mc;
-            const int64_t idx2 = ((d2 * W) * g.Mc + (row2 - d2 * g.Mc)) * g.N + col;
+            const int64_t idx2 = (d2 * W) * g.slot + (row2 - d2 * g.Mc) * g.N + col;
             f32x4_t y, y2;
             ordered_sum2<WT, LT, SB>(a.staging, idx, idx2, stride, W, L, &y, &y2);
             store_out4(a.out, row * g.N + col, y, OUT_BF16);
@@ -252,12 +252,12 @@ __global__ __launch_bounds__(kThreads) void reduce_sub_kernel(ReduceArgs a) {
     unit_rows(g, tm, slab, &lo, &hi);
     const int C4 = g.BN / 4;
     const int64_t n4 = (hi - lo) * C4;
-    const int64_t stride = g.Mc * g.N;
+    const int64_t stride = g.slot;
     for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
         const int64_t row = lo + e / C4;
         const int64_t col = (int64_t)tn * g.BN + (e % C4) * 4;
         const int64_t d = row / g.Mc, il = row - d * g.Mc;
-        const int64_t idx = ((d * g.W + (int64_t)grp * L) * g.Mc + il) * g.N + col;
+        const int64_t idx = (d * g.W + (int64_t)grp * L) * g.slot + il * g.N + col;
         const f32x4_t s = ordered_sum<LT, LT>(a.staging, idx, stride, L, L);
         float *dst = a.sub + ((d * G + grp) * g.Mc + il) * g.N + col;
         __builtin_nontemporal_store(s, (f32x4_t *)dst);

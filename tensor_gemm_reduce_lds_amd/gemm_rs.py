@@ -62,6 +62,7 @@ class gemm_rs_info_t(ctypes.Structure):
         ("trace", ctypes.c_void_p),
         ("staging_bytes", ctypes.c_int64), ("flags_bytes", ctypes.c_int64),
         ("sub_bytes", ctypes.c_int64), ("sub_flags_bytes", ctypes.c_int64),
+        ("slot_elems", ctypes.c_int64),
     ]
 
 

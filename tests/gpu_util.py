@@ -97,7 +97,8 @@ def geometry(w: I.Workload, plan: G.Plan) -> O.Geometry:
     d = plan.desc
     return O.Geometry(w.M, w.N, w.K, w.W, plan.info.tile_m, plan.info.tile_n,
                       group_m=plan.info.group_m, swizzle=d.swizzle,
-                      order=d.order, groups=d.groups, interleave=d.interleave)
+                      order=d.order, groups=d.groups, interleave=d.interleave,
+                      staging_dtype=d.staging_dtype)
 
 
 def sync():
@@ -119,6 +120,25 @@ def run_checked(plan: G.Plan, dev, w: I.Workload, out, run_flags=G.RUN_ALL,
 def flags(plan: G.Plan) -> np.ndarray:
     W, T = plan.desc.W, plan.info.T
     return d2h(plan.info.flags, plan.info.flags_bytes, np.uint32).reshape(W, T)
+
+
+def staging_slots(plan: G.Plan, geom: O.Geometry, dtype=np.float32) -> np.ndarray:
+    """The used part of every staging slot, as [W(d)][W(r)][Mc][N] (slots
+    are geom.slot elements apart; the rest of a slot is never written)."""
+    W, used = geom.W, geom.Mc * geom.N
+    assert plan.info.slot_elems == geom.slot
+    assert plan.info.staging_bytes == W * W * geom.slot * np.dtype(dtype).itemsize
+    st = d2h(plan.info.staging, plan.info.staging_bytes, dtype).reshape(W * W, geom.slot)
+    return st[:, :used].reshape(W, W, geom.Mc, geom.N)
+
+
+def put_staging(plan: G.Plan, geom: O.Geometry, S: np.ndarray) -> None:
+    """Write S[d][r][Mc][N] into the staging slots (host to device)."""
+    W, used = geom.W, geom.Mc * geom.N
+    assert plan.info.slot_elems == geom.slot
+    full = np.zeros((W * W, geom.slot), dtype=S.dtype)
+    full[:, :used] = S.reshape(W * W, used)
+    h2d(plan.info.staging, full)
 
 
 def staging_rows(plan: G.Plan, geom: O.Geometry, d: int, r: int, il0: int, n: int):

@@ -15,7 +15,8 @@ from tensor_gemm_reduce_lds_amd import gemm_rs as G
 from tensor_gemm_reduce_lds_amd import inputs as I
 
 from gpu_util import (check_bf16_staging, d2h, desc_fields, flags, geometry, h2d, hip,
-                      new_out, oracle_kw, out_bits, out_to_f64, run_checked, say, to_device)
+                      new_out, oracle_kw, out_bits, out_to_f64, run_checked, say, staging_slots,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +52,9 @@ def test_small_parity(name, w, over):
     say("bf16 staging", name)
     dev = to_device(x, w)
     with G.Plan(**desc_fields(w, **BF, **over)) as plan:
-        assert plan.info.staging_bytes == w.W * w.M * w.N * 2
+        geom = geometry(w, plan)
+        assert plan.info.slot_elems == geom.slot
+        assert plan.info.staging_bytes == w.W * w.W * geom.slot * 2
         out = new_out(w)
         run_checked(plan, dev, w, out)
         assert not flags(plan).any()
@@ -93,7 +96,7 @@ def test_integer_inputs_bit_exact(name):
         assert hip().hipMemset(ptr, 0xFF, nbytes) == 0
         out = new_out(w)
         run_checked(plan, dev, w, out, G.RUN_GEMM)
-        st = d2h(ptr, nbytes, np.uint16)
+        st = staging_slots(plan, geom, np.uint16)
         assert not (st == 0xFFFF).any(), "staging elements left unwritten"
         del st
         rows = _sample_rows(w, rng)
@@ -146,6 +149,7 @@ def test_reduce_only_widening_and_order():
     W, M, N = 2, 64, 128
     with G.Plan(M=M, N=N, K=64, W=W, tile_m=64, tile_n=128, **BF) as plan:
         Mc = M // W
+        assert plan.info.slot_elems == Mc * N            # small slots: contiguous
         S = np.empty((W, W, Mc, N), dtype=np.uint16)     # S[d][r][il][j]
         S[:, 0] = 0x4380
         S[:, 1] = 0x4382

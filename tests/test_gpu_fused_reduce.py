@@ -16,7 +16,7 @@ from tensor_gemm_reduce_lds_amd import inputs as I
 
 from gpu_util import (check_bf16_staging, check_tolerance, d2h, desc_fields, flags, geometry,
                       hip, new_out, oracle_kw, out_bits, out_to_f64, run_checked, say,
-                      to_device)
+                      staging_slots, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -154,7 +154,7 @@ def test_fused_integer_inputs_staging_footprint(name):
         out = new_out(w)
         run_checked(plan, dev, w, out, FUSED)
         assert not flags(plan).any()
-        st = d2h(ptr, nbytes, np.float32).reshape(w.W, w.W, geom.Mc, w.N)
+        st = staging_slots(plan, geom)
         bits = out_bits(out)
         assert np.array_equal(bits, out_bits(ref))
     Mc = geom.Mc

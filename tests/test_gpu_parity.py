@@ -13,7 +13,7 @@ from tensor_gemm_reduce_lds_amd import inputs as I
 
 from gpu_util import (check_tolerance, d2h, desc_fields, flags, geometry, h2d,
                       new_out, oracle_kw, out_bits, out_to_f64, run_checked, say,
-                      staging_rows, sync, to_device)
+                      staging_rows, staging_slots, sync, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,6 +151,23 @@ def test_tile_order_matches_oracle_bit_exact(name, over):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("staging", [G.STAGING_F32, G.STAGING_BF16])
+@pytest.mark.parametrize("name", ["llama8b", "llama70b", "decode", "ragged_2lvl"])
+def test_staging_slot_layout_matches_rule(name, staging):
+    """The plan's slot size and staging size follow the layout rule the
+    oracle restates (padded slots only where a slot holds 8 MiB or more:
+    the 1000-row chunks of the ragged shard)."""
+    w = W70[name]
+    say("staging layout", name, staging)
+    with G.Plan(**desc_fields(w, staging_dtype=staging)) as plan:
+        geom = geometry(w, plan)
+        eb = 2 if staging == G.STAGING_BF16 else 4
+        assert plan.info.slot_elems == geom.slot == O.staging_slot_elems(geom.Mc, w.N, eb)
+        assert plan.info.staging_bytes == w.W * w.W * geom.slot * eb
+        if name == "ragged_2lvl":
+            assert geom.slot > geom.Mc * w.N
+
+
 @pytest.mark.parametrize("swizzle", [G.SWIZZLE_REMOTE_FIRST, G.SWIZZLE_TILE_INTERLEAVED])
 @pytest.mark.parametrize("case", ["bf16_256x256_ragged", "llama8b"])
 def test_gemm_trace_matches_oracle(case, swizzle):
@@ -248,7 +265,7 @@ def test_integer_inputs_bit_exact_everywhere(name):
         out = new_out(w)
         run_checked(plan, dev, w, out, G.RUN_GEMM)
         assert flags(plan).all()
-        st = d2h(ptr, nbytes, np.float32)
+        st = staging_slots(plan, geom)
         assert not np.isnan(st).any(), "staging elements left unwritten"
         del st
         rows = _sample_rows(w, rng, per_chunk=3)

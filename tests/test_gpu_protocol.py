@@ -9,7 +9,7 @@ import oracle as O
 from tensor_gemm_reduce_lds_amd import gemm_rs as G
 from tensor_gemm_reduce_lds_amd import inputs as I
 
-from gpu_util import (desc_fields, flags, h2d, new_out, out_bits, run_checked,
+from gpu_util import (desc_fields, flags, h2d, new_out, out_bits, put_staging, run_checked,
                       say, sync, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -107,7 +107,8 @@ def _reduce_only(W, M, N, dtype, order, groups, S_rmn, tile=(64, 128),
         Mc = M // W
         # staging S[d][r][Mc][N] from S_rmn[r][d*Mc + il][j]
         st = S_rmn.reshape(W, W, Mc, N).transpose(1, 0, 2, 3)
-        h2d(plan.info.staging, np.ascontiguousarray(st, dtype=np.float32))
+        geom = O.Geometry(M, N, 64, W, tile[0], tile[1], order=order, groups=groups)
+        put_staging(plan, geom, np.ascontiguousarray(st, dtype=np.float32))
         h2d(plan.info.flags, np.ones(W * plan.info.T, dtype=np.uint32))
         out = torch.empty((M, N), dtype=torch.int16 if dtype == G.BF16 else torch.float32,
                           device="cuda:0")

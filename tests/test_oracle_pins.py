@@ -479,6 +479,49 @@ def test_staging_offset_hand_values():
     assert G.staging_offset(1, 1, 3, 2) == 4 * 2 * 3 - 1
 
 
+def test_staging_slot_size_hand_values():
+    # below 8 MiB a slot is exactly Mc*N elements
+    assert O.staging_slot_elems(2, 3, 4) == 6
+    assert O.staging_slot_elems(8, 8192, 4) == 8 * 8192
+    assert O.staging_slot_elems(255, 8192, 4) == 255 * 8192          # 7.97 MiB
+    # 8 MiB and 32 MiB are already multiples of 512 KiB
+    assert O.staging_slot_elems(256, 8192, 4) == 256 * 8192
+    assert O.staging_slot_elems(1024, 8192, 4) == 1024 * 8192
+    # 1000 rows of 8192 fp32 = 32,768,000 B = 62.5 x 512 KiB -> 63 x 512 KiB
+    # = 33,030,144 B = 8,257,536 floats (1008 rows)
+    assert O.staging_slot_elems(1000, 8192, 4) == 8257536
+    # the same rows in bfloat16: 16,384,000 B = 31.25 x 512 KiB -> 32 x
+    # 512 KiB = 16 MiB = 8,388,608 halves (1024 rows)
+    assert O.staging_slot_elems(1000, 8192, 2) == 8388608
+    # the rounding adds less than 512 KiB and never shrinks a slot
+    for Mc, N, eb in [(1000, 8192, 4), (513, 4096, 4), (4097, 1000, 2), (3, 2**21, 4)]:
+        s = O.staging_slot_elems(Mc, N, eb)
+        assert Mc * N <= s and (s - Mc * N) * eb < 512 << 10
+        if Mc * N * eb >= 8 << 20:
+            assert (s * eb) % (512 << 10) == 0
+
+
+def test_padded_staging_offsets():
+    # M=8000, W=8: Mc=1000, slots 8,257,536 floats apart (1008 rows of
+    # 8192); row il of slot (d, r) starts il*8192 after the slot's start
+    G = O.Geometry(8000, 8192, 64, 8, 256, 256)
+    assert G.slot == 8257536
+    assert G.staging_offset(0, 0, 0, 0) == 0
+    assert G.staging_offset(0, 1, 0, 0) == 8257536
+    assert G.staging_offset(0, 0, 999, 8191) == 999 * 8192 + 8191
+    # row 1000 is chunk 1's first row: slot (1, 0) = the 8th slot
+    assert G.staging_offset(1, 0, 1000, 5) == 8 * 8257536 + 5
+    assert G.staging_offset(7, 7, 7999, 8191) == 63 * 8257536 + 999 * 8192 + 8191
+    # every used element has its own offset and the slots never overlap
+    last = [G.staging_offset(d, r, d * 1000 + 999, 8191) for d in range(8) for r in range(8)]
+    first = [G.staging_offset(d, r, d * 1000, 0) for d in range(8) for r in range(8)]
+    assert first == [k * 8257536 for k in range(64)]
+    assert all(l < f for l, f in zip(last, first[1:]))
+    # bfloat16 staging pads to 1024 rows
+    Gb = O.Geometry(8000, 8192, 64, 8, 256, 256, staging_dtype=O.STAGING_BF16)
+    assert Gb.staging_offset(1, 2, 1001, 3) == (8 + 2) * 8388608 + 8192 + 3
+
+
 def test_sub_offsets_are_a_bijection():
     # sub[d][G][Mc][N]: every (destination, group, chunk row, column) has
     # its own element, and together they fill G*M*N elements exactly once
