@@ -9,8 +9,8 @@ import oracle as O
 from tensor_gemm_reduce_lds_amd import gemm_rs as G
 from tensor_gemm_reduce_lds_amd import inputs as I
 
-from gpu_util import (desc_fields, flags, h2d, new_out, out_bits, put_staging, run_checked,
-                      say, sync, to_device)
+from gpu_util import (check_tolerance, desc_fields, flags, h2d, new_out, oracle_kw, out_bits,
+                      out_to_f64, put_staging, run_checked, say, sync, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +198,57 @@ def test_overlapped_reduce_matches_serial_bits(name, swizzle):
                  G.RUN_ALL | G.OVERLAP_REDUCE | G.KEEP_FLAGS)
         assert plan.status(s)[0] == G.OK
         assert flags(plan).all()
+
+
+def _chunk_rows(w, rng, per_chunk=3):
+    """Every chunk's first and last row plus random rows of each chunk."""
+    Mc = w.M // w.W
+    rows = set()
+    for d in range(w.W):
+        rows.update([d * Mc, d * Mc + Mc - 1])
+        rows.update(d * Mc + int(v) for v in rng.integers(0, Mc, size=per_chunk - 2))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["llama70b", "ragged_2lvl"])
+def test_identity_overlap_full_size_against_oracle(name):
+    """The identity order's overlapped reduce (chunk groups reduced on the
+    plan's second stream while the next group's GEMM runs), at full size in
+    the launch configuration the benchmark times: sampled rows and 3000
+    sampled elements against the oracle's fp64 reference, then integer
+    inputs whose sampled rows must equal the oracle's emulation bit for
+    bit."""
+    import torch
+    w = I.WORKLOADS[name]
+    rng = np.random.default_rng(41)
+    kw = oracle_kw(w)
+    for dist in ("normal", "ternary"):
+        x = I.make_inputs(w) if dist == "normal" else I.make_inputs(w, dist="ternary",
+                                                                    c_dist="ternary")
+        dev = to_device(x, w)
+        say("identity overlap full", name, dist)
+        with G.Plan(**desc_fields(w, swizzle=G.SWIZZLE_IDENTITY)) as plan:
+            s = torch.cuda.current_stream()
+            got = new_out(w)
+            plan.run(dev["A"], dev["B"], dev["C"], w.alpha, w.beta, got, s,
+                     G.RUN_ALL | G.OVERLAP_REDUCE)
+            rc, detail = plan.status(s)
+            assert rc == G.OK, detail
+            assert not flags(plan).any()
+        rows = _chunk_rows(w, rng)
+        if dist == "normal":
+            g = out_to_f64(got, w)
+            ref = np.concatenate([O.reference_rows(x["A"], x["B"], x["C"], row_lo=i,
+                                                   row_hi=i + 1, **kw) for i in rows])
+            check_tolerance(g[rows], ref, w.dtype)
+            ii = rng.integers(0, w.M, size=3000)
+            jj = rng.integers(0, w.N, size=3000)
+            mx, rf = check_tolerance(g[ii, jj], O.reference_elems(x["A"], x["B"], x["C"],
+                                                                  ii=ii, jj=jj, **kw), w.dtype)
+            say("  sampled max_norm_err %.3e rel_F %.3e" % (mx, rf))
+        else:
+            bits = out_bits(got)
+            for i in rows:
+                em = O.emulate_rows(x["A"], x["B"], x["C"], row_lo=i, row_hi=i + 1, **kw)
+                assert np.array_equal(bits[i], em[0].view(bits.dtype)), i
+        del dev, got
