@@ -291,6 +291,7 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
     r.units_per_tile = p->units_per_tile;
     r.timeout_ticks = p->timeout_ticks;
     r.staging = p->staging;
+    r.staging_bytes = p->staging_bytes;
     r.staging_bf16 = p->d.staging_dtype == GEMM_RS_STAGING_BF16;
     r.out = out;
     r.flags = p->flags;

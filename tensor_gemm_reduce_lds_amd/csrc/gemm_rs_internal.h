@@ -253,6 +253,7 @@ struct ReduceArgs {
     int32_t units_per_tile;  // BM / kReduceRows
     uint64_t timeout_ticks;  // device wall-clock ticks
     const void *staging;     // float, or bfloat16 bits (staging_bf16)
+    int64_t staging_bytes;   // the whole staging (W*W slots)
     int32_t staging_bf16;
     void *out;               // [M][N]
     uint32_t *flags;         // [W][T]

@@ -383,3 +383,36 @@ def test_llama70b_other_tiles_sampled(tile):
     jj = rng.integers(0, w.N, size=2000)
     ref = O.reference_elems(x["A"], x["B"], x["C"], ii=ii, jj=jj, **oracle_kw(w))
     check_tolerance(got[ii, jj], ref, w.dtype)
+
+
+def test_staging_of_4gib_uses_64bit_slot_loads():
+    """A staging of 2^32 bytes (W=8, M=16384, N=8192) is past what the
+    reduce's 32-bit buffer offsets reach, so the reduce reads the slots
+    through 64-bit pointers, and the epilogue's slot offsets pass 2^31
+    elements: integer inputs must give the oracle's emulated bits on every
+    chunk's first and last row and on random rows, and Gaussian inputs the
+    parity bar on sampled elements."""
+    w = I.with_shape(W70["llama70b"], M=16384, K=128)
+    rng = np.random.default_rng(9)
+    kw = oracle_kw(w)
+    for dist in ("ternary", "normal"):
+        x = I.make_inputs(w, dist=dist, c_dist=dist) if dist == "ternary" else I.make_inputs(w)
+        say("4 GiB staging", dist)
+        dev = to_device(x, w)
+        with G.Plan(**desc_fields(w)) as plan:
+            assert plan.info.staging_bytes == 1 << 32
+            out = new_out(w)
+            run_checked(plan, dev, w, out)
+            assert not flags(plan).any()
+            bits = out_bits(out) if dist == "ternary" else None
+            got = out_to_f64(out, w) if dist == "normal" else None
+        del dev, out
+        if dist == "ternary":
+            for i in _sample_rows(w, rng, per_chunk=3):
+                em = O.emulate_rows(x["A"], x["B"], x["C"], row_lo=i, row_hi=i + 1, **kw)
+                assert np.array_equal(bits[i], em[0].view(bits.dtype)), i
+        else:
+            ii = rng.integers(0, w.M, size=2000)
+            jj = rng.integers(0, w.N, size=2000)
+            ref = O.reference_elems(x["A"], x["B"], x["C"], ii=ii, jj=jj, **kw)
+            check_tolerance(got[ii, jj], ref, w.dtype)
