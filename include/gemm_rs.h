@@ -227,16 +227,16 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
  * GEMM_RS_LAST_ARRIVER (both RUN bits; bf16, 256x256 tiles, W = 8, flat or
  * register two-level reduce; not with OVERLAP_REDUCE, which is
  * INVALID_ARG; otherwise the serial path): the whole pass is one GEMM
- * launch in any tile order.  Every producer stages its partial, publishes
- * its tile flag after an agent-scope release (its stores written back past
- * its XCD's L2) and counts itself in on the tile's counter with an
- * agent-scope acquire-release add.  The producer that completes the count
- * (page "flux实现：sm80 gemm+rs", section "device side barrier": the
- * counter whose last arrival ends the wait) checks and resets the tile's
- * flags and counter and sums the tile's W partials in the reduce order
- * (its own from registers) into `out`.  No workgroup waits for another,
- * so it cannot deadlock whatever the residency; each producer pays the
- * release.
+ * launch in any tile order.  Every producer stages its partial (written
+ * through its XCD's L2 when the staging is below 4 GiB), publishes its
+ * tile flag after an agent-scope release and counts itself in on the
+ * tile's counter with a relaxed agent-scope add.  The producer that
+ * completes the count (page "flux实现：sm80 gemm+rs", section "device side
+ * barrier": the counter whose last arrival ends the wait) takes an
+ * agent-scope acquire, checks and resets the tile's flags and counter and
+ * sums the tile's W partials in the reduce order (its own from registers)
+ * into `out`.  No workgroup waits for another, so it cannot deadlock
+ * whatever the residency; each producer pays the release.
  * Results are bit-identical to the serial order.
  * The caller owns A, B, C, out and the stream, and keeps them alive until
  * the stream's work is done.  Calls on one stream are ordered; one plan

@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 #pragma clang diagnostic ignored "-Winline-asm"
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, `bytes`
 // records, 32-bit untyped data format.  A load at an offset of `bytes` or
@@ -69,6 +70,10 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(lds_base) : "memory", "m0");
 }
+
+// Cache policy of a buffer access: nt (streaming) and sc1 (device scope:
+// the store is written through this XCD's L2).
+constexpr int kPolicyNtSc1 = 2 | 16;
 
 // A workgroup barrier for LDS hand-offs only: it waits for this wave's LDS
 // operations but not for its global stores, which __syncthreads would also
@@ -382,6 +387,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // its stores).  Each mode is separate code: a C load issued behind
     // stores would have to wait for all of them (memory operations complete
     // in order), so no load sits between two stores.
+    // one staged row piece: a streaming store, or with stage_wt (the
+    // last-arriver launch, FW > 0 only) a streaming device-scope buffer
+    // store through the staging descriptor
+    auto stage_store = [&](f32x4_t x, float *dst) __attribute__((always_inline)) {
+        bool wt = false;
+        if constexpr (FW > 0) wt = a.stage_wt != 0;
+        if (wt) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                a.staging, (short)0, (int)(uint32_t)a.staging_bytes, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, x), rs,
+                (int)(uint32_t)((const char *)dst - (const char *)a.staging), 0, kPolicyNtSc1);
+        } else {
+            __builtin_nontemporal_store(x, (f32x4_t *)dst);
+        }
+    };
     auto epilogue = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
         float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // the bias row's 4 columns, widened
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                                 ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
                         __builtin_nontemporal_store(hw, (u32x2_t *)((uint16_t *)a.staging + off));
                     } else {
-                        __builtin_nontemporal_store(x, (f32x4_t *)((float *)a.staging + off));
+                        stage_store(x, (float *)a.staging + off);
                     }
                 }
             }
@@ -518,7 +539,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                             if (add_c)
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
-                            __builtin_nontemporal_store(x, (f32x4_t *)dst);
+                            stage_store(x, dst);
                         }
                     }
                 } else {
@@ -721,19 +742,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         if (tid == 0 && a.trace) a.trace[b] = t;
 
         // ---- last-arriver reduce ----
-        // Each producer counts itself in on the tile's counter (an agent-scope
-        // acquire-release add, after its flag); the one that completes the
-        // count is the tile's last producer, so every partial of the tile is
-        // staged and released.  It takes the acquire, checks and resets the
-        // tile's W flags and the counter, and sums the tile as the owner-fused
-        // epilogue does (its own partial from registers).  No workgroup ever
-        // waits for another, so residency cannot deadlock it.
+        // Each producer counts itself in on the tile's counter (a relaxed
+        // agent-scope add, after its release and flag); the one that
+        // completes the count is the tile's last producer, so every partial
+        // of the tile is staged and released.  It takes the acquire, checks
+        // and resets the tile's W flags and the counter, and sums the tile as
+        // the owner-fused epilogue does (its own partial from registers).  No
+        // workgroup ever waits for another, so residency cannot deadlock it.
         if constexpr (FW > 0) if (a.fuse_reduce == kFuseLastArriver) {
             int last = 0;
             if (tid == 0) {
-                const uint32_t old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_ACQ_REL,
+                // relaxed: the release fence before the flag orders this
+                // producer's stores before its count, and every add extends
+                // the release sequence the last one reads; only the last
+                // producer needs the acquire (an L2 invalidate), not each one
+                const uint32_t old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT);
-                if (old == (uint32_t)FW - 1) last = 1;
+                if (old == (uint32_t)FW - 1) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    last = 1;
+                }
                 else if (old >= (uint32_t)FW) record_error(a.err, GEMM_RS_ERR_PROTOCOL, r, t, old);
             }
             if (!__syncthreads_or(last)) return;

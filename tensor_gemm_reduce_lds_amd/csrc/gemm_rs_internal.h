@@ -212,6 +212,11 @@ struct GemmArgs {
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
     int32_t release_flags;  // 1: agent-scope release before the flag (consumer in this launch)
+    // 1: staging stores written through this XCD's L2 (`nt sc1` buffer
+    // stores through one descriptor of staging_bytes < 4 GiB), so the
+    // release before each flag finds no dirty staging lines to write back
+    int32_t stage_wt;
+    int64_t staging_bytes;
     // (rank << 26) | tile of every slot of the full launch (b_offset 0,
     // n_blocks W*T, the XCD map), tabulated once per plan; null: derive it
     // with logical_block and tile_of_block (launch slices, no plan)
