@@ -718,20 +718,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         else epilogue(std::integral_constant<int, 2>{});
 
         // ---- publish: all stores of this tile, then flag[r][t] = 1 ----
-        // With a consumer in the same launch (the last-arriver reduce) the flag
-        // follows an agent-scope release: the tile's stores are written back
-        // past this XCD's L2 before it.  When the consumer is stream-ordered
-        // after this kernel, the kernel boundary already makes the stores
-        // visible and the flag is a plain store.
+        // With a consumer in the same launch (the last-arriver reduce) the
+        // flag and the tile's stores are released together, by the release
+        // fence ahead of the producer's count below: the fence comes after
+        // the flag store, so the count orders both.  When the consumer is
+        // stream-ordered after this kernel, the kernel boundary already makes
+        // the stores visible and the flag is a plain store.
         if (!a.flags) {
             // all-gather mode: an ordinary output tile, no flag
         } else if (a.release_flags) {
             __syncthreads();                            // every wave's stores are done
-            if (tid == 0) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (tid == 0)
                 __hip_atomic_store(&a.flags[(int64_t)r * g.T + t], 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            }
         } else {
             // the consumer runs after this kernel has completed, so the flag
             // needs no ordering against the other waves' stores here
@@ -742,20 +741,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         if (tid == 0 && a.trace) a.trace[b] = t;
 
         // ---- last-arriver reduce ----
-        // Each producer counts itself in on the tile's counter (a relaxed
-        // agent-scope add, after its release and flag); the one that
-        // completes the count is the tile's last producer, so every partial
-        // of the tile is staged and released.  It takes the acquire, checks
-        // and resets the tile's W flags and the counter, and sums the tile as
-        // the owner-fused epilogue does (its own partial from registers).  No
-        // workgroup ever waits for another, so residency cannot deadlock it.
+        // Each producer counts itself in on the tile's counter (an
+        // agent-scope release fence, then a relaxed add, after its stores and
+        // its flag); the one that completes the count is the tile's last
+        // producer, so every partial of the tile is staged and released.  It
+        // takes the acquire, checks and resets the tile's W flags and the
+        // counter, and sums the tile as the owner-fused epilogue does (its own
+        // partial from registers).  No workgroup ever waits for another, so
+        // residency cannot deadlock it.
         if constexpr (FW > 0) if (a.fuse_reduce == kFuseLastArriver) {
             int last = 0;
             if (tid == 0) {
-                // relaxed: the release fence before the flag orders this
-                // producer's stores before its count, and every add extends
-                // the release sequence the last one reads; only the last
-                // producer needs the acquire (an L2 invalidate), not each one
+                // The release fence orders everything before it in this
+                // workgroup (every wave's staging stores, by the barrier
+                // above, and the flag) before the add; every add extends
+                // the release sequence the last one reads, so its acquire
+                // fence sees all W producers' stores and flags.  Only the
+                // last producer pays the acquire (an L2 invalidate).
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                 const uint32_t old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT);
                 if (old == (uint32_t)FW - 1) {

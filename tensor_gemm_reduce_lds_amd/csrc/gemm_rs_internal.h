@@ -211,7 +211,8 @@ struct GemmArgs {
     int32_t staging_bf16;   // 1: stage partials as bfloat16 (round to nearest even)
     uint32_t *flags;     // [W][T]
     int32_t *trace;      // [W*T] or null
-    int32_t release_flags;  // 1: agent-scope release before the flag (consumer in this launch)
+    int32_t release_flags;  // 1: the flag is read in this launch (last-arriver): it is
+                            //    stored after a barrier and released with the count
     // 1: staging stores written through this XCD's L2 (`nt sc1` buffer
     // stores through one descriptor of staging_bytes < 4 GiB), so the
     // release before each flag finds no dirty staging lines to write back
