@@ -122,7 +122,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int A_ROWS = 1024 / (BK * 2);       // A rows per 1 KB
     constexpr int CPR = BN / 8;                   // 16-byte chunks per B row
     constexpr int B_ROWS = 1024 / (BN * 2);       // B rows per 1 KB
-    constexpr int PER = A_ISSUES + B_ISSUES;      // DMA loads per lane per stage
     static_assert(A_ISSUES * NW * 1024 == A_BYTES && B_ISSUES * NW * 1024 == B_BYTES, "");
     static_assert(CPR >= 16, "B swizzle needs rows of at least 16 chunks");
 
@@ -189,31 +188,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     const int64_t a_rows = g.M - row0 < BM ? g.M - row0 : BM;
     const uint32_t a_bytes = (uint32_t)(((a_rows - 1) * g.K + BK) * 2);
     const uint32_t b_bytes = (uint32_t)(((int64_t)(BK - 1) * g.N + BN) * 2);
-    uint32_t a_voff[A_ISSUES];
+    // With 8 waves the operand DMA is issued by waves 0..3 only, one per
+    // SIMD (wave w runs on SIMD w % 4), each with twice the loads: every
+    // SIMD then has one wave that only reads LDS fragments and issues
+    // MFMAs, which keeps the matrix pipe fed while the other wave issues
+    // the DMA (measured +3% on the 70B-like shard, +2-6% on the 8B-like).
+    constexpr int DW = NW >= 8 ? NW / 2 : NW;     // waves that issue the DMA
+    constexpr int AI = A_ISSUES * NW / DW, BI = B_ISSUES * NW / DW;
+    static_assert(AI * DW == A_ISSUES * NW && BI * DW == B_ISSUES * NW, "");
+    const int dwave = wave < DW ? wave : 0;
+    uint32_t a_voff[AI];
 #pragma unroll
-    for (int i = 0; i < A_ISSUES; ++i) {
-        const int m = (i * NW + wave) * A_ROWS + lane / CPA;
+    for (int i = 0; i < AI; ++i) {
+        const int m = (i * DW + dwave) * A_ROWS + lane / CPA;
         const int64_t ml = m < a_rows ? m : a_rows - 1;   // ragged M: fetch a valid row
         a_voff[i] = (uint32_t)((ml * g.K + ((lane % CPA) ^ swa<BK>(m)) * 8) * 2);
     }
-    uint32_t b_voff[B_ISSUES];
+    uint32_t b_voff[BI];
 #pragma unroll
-    for (int i = 0; i < B_ISSUES; ++i) {
-        const int k = (i * NW + wave) * B_ROWS + lane / CPR;
+    for (int i = 0; i < BI; ++i) {
+        const int k = (i * DW + dwave) * B_ROWS + lane / CPR;
         b_voff[i] = (uint32_t)(((int64_t)k * g.N + ((lane % CPR) ^ swb(k)) * 8) * 2);
     }
 
     auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+        if (wave >= DW) return;                     // wave-uniform
         const uint32_t As = smem_base + buf * STAGE;
         const uint32_t Bs = As + A_BYTES;
         const i32x4_t a_rsrc = buffer_rsrc(A + row0 * g.K + (int64_t)kt * BK, a_bytes);
         const i32x4_t b_rsrc = buffer_rsrc(B + (int64_t)kt * BK * g.N + col0, b_bytes);
 #pragma unroll
-        for (int i = 0; i < A_ISSUES; ++i)
-            dma16(a_rsrc, a_voff[i], As + (i * NW + wave) * 1024);
+        for (int i = 0; i < AI; ++i)
+            dma16(a_rsrc, a_voff[i], As + (i * DW + dwave) * 1024);
 #pragma unroll
-        for (int i = 0; i < B_ISSUES; ++i)
-            dma16(b_rsrc, b_voff[i], Bs + (i * NW + wave) * 1024);
+        for (int i = 0; i < BI; ++i)
+            dma16(b_rsrc, b_voff[i], Bs + (i * DW + dwave) * 1024);
     };
 
     // ---- per-lane LDS read offsets (bytes, within a stage) ----
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         // may stay in flight); the barrier makes every wave's data visible
         // and frees the stage read in step kt-1 for the next issue
         const int ahead = KT - 1 - kt;
-        wait_groups<PER, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
+        wait_groups<AI + BI, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
         __syncthreads();
         lds_char *S = smem + (kt % STAGES) * STAGE;
         load_frags(S, 0, af[0], bfr[0]);
