@@ -9,7 +9,9 @@
 //     LDS stages; loads run STAGES-1 steps ahead of the MFMAs.  The DMA is
 //     issued from inline asm and its completion tracked by explicit vmcnt
 //     waits, so the compiler does not serialise LDS reads of one stage
-//     behind DMA still in flight into another.
+//     behind DMA still in flight into another.  With 8 waves only one
+//     wave per SIMD issues it, so the other wave of each SIMD only feeds
+//     the matrix pipe.
 //   * A sits in LDS as [m][k] rows of 2*BK bytes; B stays row-major [k][n]
 //     as it is in memory.  Both are XOR-swizzled at 16-byte granularity
 //     (the swizzle is applied by choosing which global chunk each lane
@@ -18,7 +20,8 @@
 //     ds_read_b64_tr_b16 per MFMA, which transpose 4x16 bf16 blocks across
 //     16 lanes so that each lane gets 4 consecutive k of one column.
 //   * v_mfma_f32_32x32x16_bf16, fp32 accumulators; the LDS reads of the
-//     next 16-deep slice are interleaved with the MFMAs of the current one.
+//     next 16-deep slice are interleaved with the MFMAs of the current one,
+//     and each step's last slice is issued after the next step's barrier.
 // Epilogue: alpha*acc, plus beta*C on rows whose chunk this rank owns,
 // stored as fp32 (or, optionally, rounded to bf16) into the staging slot
 // of each row's destination chunk
@@ -26,7 +29,8 @@
 // staging rows); then the tile's ready flag is published (page "flux实现：
 // sm80 gemm+rs", section "cutlass自定义epilogue–sm80": a compute node
 // alpha*acc + beta*C, a store node that scatters by destination, and a
-// per-tile flag).
+// per-tile flag).  The FW instantiation also sums tiles in place of the
+// separate reduce: the owner-fused last step and the last-arriver launch.
 #include <mutex>
 #include <type_traits>
 
