@@ -48,6 +48,10 @@ CASES = [
      G.RUN_ALL | G.OVERLAP_REDUCE),
     ("bf16_staging", I.with_shape(W70["llama8b"], M=256, N=512, K=128),
      dict(staging_dtype=G.STAGING_BF16), G.RUN_ALL),
+    # the one-launch last-arriver pass (write-through staging stores into
+    # the array, release and count per producer, the last one sums)
+    ("last_arriver", I.with_shape(W70["llama70b"], M=1024, N=512, K=128),
+     dict(tile_m=256, tile_n=256), G.RUN_ALL | G.LAST_ARRIVER),
 ]
 
 
