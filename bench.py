@@ -333,6 +333,13 @@ def main():
     ap.add_argument("--ag-only", action="store_true",
                     help="time only the all-gather + GEMM half and print its object "
                          "(profiling runs of that path)")
+    ap.add_argument("--soak", type=float, default=0.0,
+                    help="seconds: only run --soak-kernel back to back for this long after "
+                         "a warm-up (board power and clocks can then be sampled from "
+                         "outside) and print its launch rate")
+    ap.add_argument("--soak-kernel", default="gemm", choices=["gemm", "step", "bmm"],
+                    help="what --soak runs: the GEMM launch, the serial step (GEMM and "
+                         "reduce), or torch.bmm on the same GEMMs (hipBLASLt, context)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="MiB: run one plain device copy of this size first "
                          "(reference point for HBM byte counters)")
@@ -385,6 +392,43 @@ def main():
         torch.cuda.synchronize()
         log("bench: calibration copy of %d MiB done" % args.copy_calibration)
         del src, dst
+
+    if args.soak > 0:
+        if args.soak_kernel == "bmm":
+            if w.dtype != "bf16":
+                raise SystemExit("--soak-kernel bmm needs a bf16 workload")
+            Ab = A.view(torch.bfloat16)
+            Bb = B.view(torch.bfloat16).contiguous()
+            Cb = torch.empty((w.W, w.M, w.N), dtype=torch.bfloat16, device=dev)
+            one = lambda: torch.bmm(Ab, Bb, out=Cb)
+        else:
+            # the GEMM alone sets every flag again each launch; one reduce
+            # after the loop puts them back
+            flags = G.RUN_GEMM if args.soak_kernel == "gemm" else G.RUN_ALL
+            one = lambda: plan.run(A, B, C, w.alpha, w.beta, out, stream, flags)
+        for _ in range(max(args.warmup, 1)):
+            one()
+        torch.cuda.synchronize()
+        log("soak: running %s for %.0f s" % (args.soak_kernel, args.soak))
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.soak:
+            for _ in range(20):
+                one()
+            torch.cuda.synchronize()
+            n += 20
+        dt = time.perf_counter() - t0
+        if args.soak_kernel == "gemm":
+            plan.run(A, B, C, w.alpha, w.beta, out, stream, G.RUN_REDUCE)
+        if args.soak_kernel != "bmm":
+            rc, detail = plan.status(stream)
+            if rc != G.OK:
+                raise RuntimeError("soak run failed: %s %s" % (G.gemm_rs_strerror(rc), detail))
+        log("soak: done")
+        print(json.dumps({"soak": {"workload": w.name, "kernel": args.soak_kernel,
+                                   "seconds": round(dt, 2), "iterations": n,
+                                   "ms_per_iteration": round(dt * 1e3 / n, 4)}}), flush=True)
+        plan.close()
+        return
 
     if args.fused_only:
         # warm-up, then the timed owner-fused steps with HIP events around
