@@ -79,6 +79,29 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_
 // the store is written through this XCD's L2).
 constexpr int kPolicyNtSc1 = 2 | 16;
 
+// Four bfloat16 values (lo holds the first two, low half first) widened
+// exactly to floats: a bfloat16 is the top half of a float.
+__device__ __forceinline__ f32x4_t widen_bf16x4(uint32_t lo, uint32_t hi) {
+    f32x4_t v;
+    v[0] = __uint_as_float(lo << 16);
+    v[1] = __uint_as_float(lo & 0xffff0000u);
+    v[2] = __uint_as_float(hi << 16);
+    v[3] = __uint_as_float(hi & 0xffff0000u);
+    return v;
+}
+
+// Four floats rounded to bfloat16 (nearest even), packed in the same layout.
+__device__ __forceinline__ u32x2_t pack_bf16x4(f32x4_t x) {
+    const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
+    const __bf16 h2 = (__bf16)x[2], h3 = (__bf16)x[3];
+    u32x2_t w;
+    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+    return w;
+}
+
 // A workgroup barrier for LDS hand-offs only: it waits for this wave's LDS
 // operations but not for its global stores, which __syncthreads would also
 // drain (its release fence covers global memory), a full memory latency.
@@ -165,11 +188,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                    a.epoch) {
                 if (wall_clock64() - t0 > a.timeout_ticks) {
                     failed = 1;
-                    if (atomicCAS(&a.err[0], 0, GEMM_RS_ERR_TIMEOUT) == 0) {
-                        __hip_atomic_store(&a.err[1], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&a.err[2], tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&a.err[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                    record_error(a.err, GEMM_RS_ERR_TIMEOUT, r, tm, 0);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(4);
@@ -363,6 +382,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     if (KT > 0) mfmas(1);   // the last step's last slice
 
     // ---- epilogue: D = alpha*acc (+ beta*C on owned rows), scatter ----
+    // beta*C is added with one fused multiply-add, in every path (plain,
+    // ragged and fused epilogues), so all of them round a staged value alike.
     // The accumulators go out through LDS one 32-row stripe at a time so
     // that every store instruction writes whole staging rows (64 lanes x
     // 16 bytes = 1 KB contiguous for BN = 256): a store pattern of 32 rows x
@@ -418,13 +439,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     };
     auto epilogue = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
-        float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // the bias row's 4 columns, widened
-        if constexpr (MODE == 1) {
-            cf[0] = __uint_as_float(cb_row.x << 16);
-            cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
-            cf[2] = __uint_as_float(cb_row.y << 16);
-            cf[3] = __uint_as_float(cb_row.y & 0xffff0000u);
-        }
+        // the bias row's 4 columns, widened
+        const f32x4_t cf = MODE == 1 ? widen_bf16x4(cb_row.x, cb_row.y) : f32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             // stage block i of every wave: stripe rows wm*32 .. +31 hold tile
@@ -473,50 +489,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                                   col0 + scol;
             auto store_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int k = 0; k < ST_PER_WAVE; ++k) {
-                const int sr = sr0 + k * RPI;               // row in the stripe set
-                const int64_t row = rowF + k * RPI;
-                f32x4_t x = *at(sr, scol >> 2);
-                if (row < g.M) {
-                    int32_t d = dF;
-                    int64_t off = offF + (int64_t)(k * RPI) * g.N;
-                    if (row >= next_chunk) {                 // a chunk boundary inside the group
-                        d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
-                        off = a.plain_out
-                                  ? ((int64_t)r * g.M + row) * g.N + col0 + scol
-                                  : (int64_t)d * slot_d + slot_r + (row - (int64_t)d * g.Mc) * g.N +
-                                        col0 + scol;
-                    }
-                    if constexpr (MODE != 0) {
-                        const uint2 cb = MODE == 1 ? cb_row : cb_full[k];
-                        const float y0 = x[0] + beta * __uint_as_float(cb.x << 16);
-                        const float y1 = x[1] + beta * __uint_as_float(cb.x & 0xffff0000u);
-                        const float y2 = x[2] + beta * __uint_as_float(cb.y << 16);
-                        const float y3 = x[3] + beta * __uint_as_float(cb.y & 0xffff0000u);
-                        const bool own = d == r;    // C counts once: on its owner's rows
-                        x[0] = own ? y0 : x[0];
-                        x[1] = own ? y1 : x[1];
-                        x[2] = own ? y2 : x[2];
-                        x[3] = own ? y3 : x[3];
-                    }
-                    // whole 128-byte lines from one instruction: a streaming
-                    // store keeps the staging from evicting the A/B panels
-                    // other tiles are still reading
-                    if (a.staging_bf16) {
-                        // bfloat16 staging: each partial rounded to nearest even
-                        const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
-                        const __bf16 h2 = (__bf16)x[2], h3 = (__bf16)x[3];
-                        u32x2_t hw;
-                        hw[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                        hw[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                        __builtin_nontemporal_store(hw, (u32x2_t *)((uint16_t *)a.staging + off));
-                    } else {
-                        stage_store(x, (float *)a.staging + off);
+                for (int k = 0; k < ST_PER_WAVE; ++k) {
+                    const int sr = sr0 + k * RPI;               // row in the stripe set
+                    const int64_t row = rowF + k * RPI;
+                    f32x4_t x = *at(sr, scol >> 2);
+                    if (row < g.M) {
+                        int32_t d = dF;
+                        int64_t off = offF + (int64_t)(k * RPI) * g.N;
+                        if (row >= next_chunk) {   // a chunk boundary inside the group
+                            d = (int32_t)((uint64_t)row / (uint64_t)g.Mc);
+                            off = a.plain_out ? ((int64_t)r * g.M + row) * g.N + col0 + scol
+                                              : (int64_t)d * slot_d + slot_r +
+                                                    (row - (int64_t)d * g.Mc) * g.N + col0 + scol;
+                        }
+                        if constexpr (MODE != 0) {
+                            const uint2 cb = MODE == 1 ? cb_row : cb_full[k];
+                            const f32x4_t c = widen_bf16x4(cb.x, cb.y);
+                            const bool own = d == r;    // C counts once: on its owner's rows
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const float yu = __builtin_fmaf(beta, c[u], x[u]);
+                                x[u] = own ? yu : x[u];
+                            }
+                        }
+                        // whole 128-byte lines from one instruction: a streaming
+                        // store keeps the staging from evicting the A/B panels
+                        // other tiles are still reading
+                        if (a.staging_bf16) {
+                            // bfloat16 staging: each partial rounded to nearest even
+                            __builtin_nontemporal_store(pack_bf16x4(x),
+                                                        (u32x2_t *)((uint16_t *)a.staging + off));
+                        } else {
+                            stage_store(x, (float *)a.staging + off);
+                        }
                     }
                 }
-            }
             };
             const int64_t rowL = rowF + (int64_t)(ST_PER_WAVE - 1) * RPI;
             if constexpr (MODE != 2) {
@@ -534,15 +541,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                             f32x4_t x = *at(sr0 + k * RPI, scol >> 2);
                             if (add_c)
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
-                            const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
-                            const __bf16 h2 = (__bf16)x[2], h3 = (__bf16)x[3];
-                            u32x2_t hw;
-                            hw[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                            hw[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                            __builtin_nontemporal_store(hw, (u32x2_t *)dst);
+                                for (int u = 0; u < 4; ++u)
+                                    x[u] = __builtin_fmaf(beta, cf[u], x[u]);
+                            __builtin_nontemporal_store(pack_bf16x4(x), (u32x2_t *)dst);
                         }
                     } else {
                         float *dst = (float *)a.staging + offF;
@@ -551,7 +552,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                             f32x4_t x = *at(sr0 + k * RPI, scol >> 2);
                             if (add_c)
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * cf[u];
+                                for (int u = 0; u < 4; ++u)
+                                    x[u] = __builtin_fmaf(beta, cf[u], x[u]);
                             stage_store(x, dst);
                         }
                     }
@@ -584,13 +586,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         const int L = FW / a.groups;                 // ranks per group
         const int64_t slot = g.slot;                 // elements from slot (d,q) to (d,q+1)
         const int q_lo = r;                          // remote j < r is rank j, else j+1
-        float cf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (MODE == 1) {
-            cf[0] = __uint_as_float(cb_row.x << 16);
-            cf[1] = __uint_as_float(cb_row.x & 0xffff0000u);
-            cf[2] = __uint_as_float(cb_row.y << 16);
-            cf[3] = __uint_as_float(cb_row.y & 0xffff0000u);
-        }
+        const f32x4_t cf = MODE == 1 ? widen_bf16x4(cb_row.x, cb_row.y) : f32x4_t{0, 0, 0, 0};
         __syncthreads();                            // every wave is done with the stages
         // the remote partials of one row (wave-uniform row for BN = 256)
         auto load_row = [&](int64_t base, raw_t (&v)[NR]) __attribute__((always_inline)) {
@@ -598,22 +594,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             for (int j = 0; j < NR; ++j) {
                 const int64_t idx = base + (int64_t)(j < q_lo ? j : j + 1) * slot;
                 if constexpr (SB)
-                    v[j] = __builtin_nontemporal_load((const u32x2_t *)((const uint16_t *)a.staging + idx));
+                    v[j] = __builtin_nontemporal_load(
+                        (const u32x2_t *)((const uint16_t *)a.staging + idx));
                 else
-                    v[j] = __builtin_nontemporal_load((const f32x4_t *)((const float *)a.staging + idx));
+                    v[j] = __builtin_nontemporal_load(
+                        (const f32x4_t *)((const float *)a.staging + idx));
             }
         };
         auto widen = [](raw_t x) -> f32x4_t {
-            if constexpr (SB) {
-                f32x4_t v;
-                v[0] = __uint_as_float(x[0] << 16);
-                v[1] = __uint_as_float(x[0] & 0xffff0000u);
-                v[2] = __uint_as_float(x[1] << 16);
-                v[3] = __uint_as_float(x[1] & 0xffff0000u);
-                return v;
-            } else {
-                return x;
-            }
+            if constexpr (SB) return widen_bf16x4(x[0], x[1]);
+            else return x;
         };
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -653,21 +643,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                 f32x4_t x = *(__attribute__((address_space(3))) f32x4_t *)(
                     smem + (sr0 + k * RPI) * EP_PITCH + scol * 4);
                 if constexpr (MODE != 0) {
-                    float c4[4];
-                    if constexpr (MODE == 1) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) c4[u] = cf[u];
-                    } else {
+                    f32x4_t c4 = cf;
+                    if constexpr (MODE == 2) {
                         const int64_t crow = row < g.M ? row : g.M - 1;
                         const uint2 cb = *(const uint2 *)(Cp + crow * a.ldc + col0 + scol);
-                        c4[0] = __uint_as_float(cb.x << 16);
-                        c4[1] = __uint_as_float(cb.x & 0xffff0000u);
-                        c4[2] = __uint_as_float(cb.y << 16);
-                        c4[3] = __uint_as_float(cb.y & 0xffff0000u);
+                        c4 = widen_bf16x4(cb.x, cb.y);
                     }
                     if (d_cur == r)                 // C counts once: on its owner's rows
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) x[u] = x[u] + beta * c4[u];
+                        for (int u = 0; u < 4; ++u) x[u] = __builtin_fmaf(beta, c4[u], x[u]);
                 }
                 if constexpr (SB) {
                     // the value a bfloat16 staging slot would hold
@@ -688,15 +672,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                     if (q % L == L - 1) y = (q / L == 0) ? sg : y + sg;
                 }
                 if (row < g.M) {
-                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
-                    const __bf16 h2 = (__bf16)y[2], h3 = (__bf16)y[3];
-                    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    const u32x2_t w = pack_bf16x4(y);
                     // written through past this XCD's L2, as the reduce does
                     __hip_atomic_store((uint64_t *)((uint16_t *)a.out + row * g.N + col0 + scol),
-                                       (uint64_t)w0 | ((uint64_t)w1 << 32), __ATOMIC_RELAXED,
+                                       (uint64_t)w[0] | ((uint64_t)w[1] << 32), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if (k + 1 < ST_PER_WAVE) {
@@ -716,7 +695,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             else fused_epilogue(std::integral_constant<int, 2>{}, std::true_type{});
         } else {
             if (!a.has_c) fused_epilogue(std::integral_constant<int, 0>{}, std::false_type{});
-            else if (a.ldc == 0) fused_epilogue(std::integral_constant<int, 1>{}, std::false_type{});
+            else if (a.ldc == 0)
+                fused_epilogue(std::integral_constant<int, 1>{}, std::false_type{});
             else fused_epilogue(std::integral_constant<int, 2>{}, std::false_type{});
         }
     };

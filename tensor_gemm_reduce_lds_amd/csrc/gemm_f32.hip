@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
         if (row >= g.M) continue;
         const int32_t d = (int32_t)((uint32_t)row / (uint32_t)g.Mc);
         float x = a.alpha * acc[v];
-        if (a.has_c && d == r) x += a.beta * Cp[row * a.ldc + col];
+        if (a.has_c && d == r) x = __builtin_fmaf(a.beta, Cp[row * a.ldc + col], x);
         float *dst = (float *)a.staging +
                      ((int64_t)d * g.W + r) * g.slot + (row - (int64_t)d * g.Mc) * g.N;
         __builtin_nontemporal_store(x, dst + col);

@@ -153,8 +153,9 @@ __host__ __device__ inline void tile_of_block(const TileGeom &g, uint32_t b,
 // evenly over the XCDs, XCD x takes the x-th eighth of every rank's part of
 // the order, rank after rank: all XCDs then work on one rank's operands at a
 // time, so the memory-side cache can serve that rank's B to every XCD after
-// one read from HBM, while each XCD's L2 keeps its own tile-rows of A.  Every rank's tile order is unchanged.  Otherwise the
-// identity.  A bijection of [0, n) in both cases.
+// one read from HBM, while each XCD's L2 keeps its own tile-rows of A.
+// Every rank's tile order is unchanged.  Otherwise the identity.  A
+// bijection of [0, n) in both cases.
 __host__ __device__ inline uint32_t logical_block(const TileGeom &g, uint32_t b_offset,
                                                   uint32_t n, uint32_t h) {
     constexpr uint32_t kXcds = 8;

@@ -403,7 +403,8 @@ hipError_t launch_flat(const ReduceArgs &a, hipStream_t s) {
     if (a.slice_kind != kSliceAll) return launch_w<BF, SB, false, false>(a, grid, s);
     // fp32 staging below 4 GiB: the slots through one buffer descriptor
     if constexpr (!SB)
-        if (a.staging_bytes <= (int64_t)0xffffffffu) return launch_w<BF, SB, true, true>(a, grid, s);
+        if (a.staging_bytes <= (int64_t)0xffffffffu)
+            return launch_w<BF, SB, true, true>(a, grid, s);
     return launch_w<BF, SB, true, false>(a, grid, s);
 }
 

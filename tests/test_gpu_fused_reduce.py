@@ -31,6 +31,17 @@ SMALL = [
     # full C matrix with alpha and beta
     ("full_c", I.with_shape(W70["llama70b"], M=2048, N=512, K=192, ldc=512,
                             alpha=1.25, beta=0.75, c_std=1.0), {}),
+    # beta*C inexact in float (beta = 0.7, 0.3): the serial epilogue's paths
+    # and the fused sum must all round x + beta*c the same way
+    ("bias_row_beta", I.with_shape(W70["llama70b"], M=2048, N=512, K=256,
+                                   alpha=1.0, beta=0.7, c_std=1.0), {}),
+    ("full_c_beta", I.with_shape(W70["llama70b"], M=2048, N=512, K=192, ldc=512,
+                                 alpha=0.9, beta=0.3, c_std=1.0), {}),
+    # the same with bfloat16 staging and tiles straddling chunks (the
+    # epilogue's ragged-row path): the staged value is rounded once more
+    ("bf16_staging_bias_beta", I.with_shape(W70["llama70b"], M=4000, N=512, K=128,
+                                            alpha=1.0, beta=0.7, c_std=1.0),
+     dict(staging_dtype=G.STAGING_BF16)),
     # Mc = 500: two tile-rows per chunk, every second one straddles into the
     # next chunk, ragged last tile-row (4000 = 15*256 + 160); two-level G=2
     ("straddle_2lvl", I.with_shape(W70["ragged_2lvl"], M=4000, N=512, K=128), {}),
