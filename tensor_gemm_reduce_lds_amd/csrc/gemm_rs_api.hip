@@ -320,7 +320,10 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
         x.slot_tab = p->slot_tab;   // the full launch
         x.fuse_reduce = kFuseLastArriver;
         x.release_flags = 1;
-        x.stage_wt = p->staging_bytes <= (int64_t)0xffffffffu && !p->d.staging_dtype ? 1 : 0;
+        // fp32 staging below 4 GiB: written through past L2 by buffer
+        // stores, so the producers' release has no dirty lines to flush
+        x.stage_wt = (p->staging_bytes <= (int64_t)0xffffffffu &&
+                      p->d.staging_dtype == GEMM_RS_STAGING_F32) ? 1 : 0;
         x.staging_bytes = p->staging_bytes;
         x.counters = p->counters;
         x.keep_flags = (run_flags & GEMM_RS_KEEP_FLAGS) ? 1 : 0;
