@@ -227,10 +227,11 @@ GEMM_RS_API int gemm_rs_plan(const gemm_rs_desc_t *desc, gemm_rs_plan_t *out);
  * GEMM_RS_LAST_ARRIVER (both RUN bits; bf16, 256x256 tiles, W = 8, flat or
  * register two-level reduce; not with OVERLAP_REDUCE, which is
  * INVALID_ARG; otherwise the serial path): the whole pass is one GEMM
- * launch in any tile order.  Every producer stages its partial (written
- * through its XCD's L2 when the staging is below 4 GiB), publishes its
- * tile flag after an agent-scope release and counts itself in on the
- * tile's counter with a relaxed agent-scope add.  The producer that
+ * launch in any tile order.  Every producer stages its partial (fp32
+ * staging below 4 GiB is written through its XCD's L2), sets its tile
+ * flag, and then counts itself in on the tile's counter with a relaxed
+ * agent-scope add behind an agent-scope release fence, which orders the
+ * staged partial and the flag before the count.  The producer that
  * completes the count (page "flux实现：sm80 gemm+rs", section "device side
  * barrier": the counter whose last arrival ends the wait) takes an
  * agent-scope acquire, checks and resets the tile's flags and counter and
