@@ -22,11 +22,12 @@ constexpr int kCopyThreads = 256;
 // per-tile-row arrival counters stay consistent across 32-bit wrap-around)
 constexpr uint32_t kSubBlocks = 16;
 static_assert((kSubBlocks & (kSubBlocks - 1)) == 0, "power of two");
-// The copies must run beside a GEMM whose resident tiles wait for them: a
-// copy wave's registers have to fit in what every GEMM tile configuration
-// leaves free on a SIMD at its own maximum occupancy (the test suite checks
-// this against the compiler's resource report; the copy loop is kept
-// shallow for it).  Workgroups of the persistent copy grid: one per CU.
+// The copy grid is enqueued before the gated GEMM, so its progress does not
+// rest on finding room beside waiting GEMM tiles; its waves still fit in the
+// registers every GEMM tile configuration leaves free on a SIMD at its own
+// maximum occupancy (the test suite checks this against the compiler's
+// resource report), so copies keep running while GEMM tiles hold the CUs.
+// Workgroups of the persistent copy grid: one per CU.
 constexpr uint32_t kCopyGrid = 256;
 
 struct AgCopyArgs {
