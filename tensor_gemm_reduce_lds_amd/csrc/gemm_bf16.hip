@@ -13,7 +13,8 @@
 //     wave per SIMD issues it, so the other wave of each SIMD only feeds
 //     the matrix pipe.
 //   * A sits in LDS as [m][k] rows of 2*BK bytes; B stays row-major [k][n]
-//     as it is in memory.  Both are XOR-swizzled at 16-byte granularity
+//     as it is in memory; LDS holds every stage's A tile, then every
+//     stage's B tile.  Both are XOR-swizzled at 16-byte granularity
 //     (the swizzle is applied by choosing which global chunk each lane
 //     fetches, since a DMA load writes lane l at base + 16*l).
 //   * A operands come from ds_read_b128; B operands from two
@@ -136,13 +137,24 @@ __device__ __forceinline__ int swa(int m) {
 __device__ __forceinline__ int swb(int k) { return 4 * (k & 3); }
 
 // FW > 0: the owner-fused reduce variant for W == FW ranks (see GemmArgs).
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW>
+// U2: the K loop unrolled by two steps, so that each step's stage is a
+// compile-time constant and its fragment reads take the stage offset in their
+// immediate field (no per-read address add; ~1% at the 70B-like shard).  It
+// needs every register of two waves per SIMD, so launches that must leave
+// room for other kernels' waves on the same CUs (the all-gather's copies,
+// the identity-order reduce slices) use the rolled loop.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW, bool U2>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int NW = WGM * WGN;                 // waves
     constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE = A_BYTES + B_BYTES;
+    // LDS holds the A tiles of all stages, then the B tiles of all stages:
+    // stage s of an operand lies s tiles past its first, an offset that fits
+    // a DS read's 16-bit immediate, so with the stage known at compile time
+    // the fragment reads need no per-read address add
+    constexpr int B_REGION = STAGES * A_BYTES;
     constexpr int A_ISSUES = A_BYTES / 1024 / NW;  // 1 KB DMA loads per wave
     constexpr int B_ISSUES = B_BYTES / 1024 / NW;
     constexpr int CPA = BK / 8;                   // 16-byte chunks per A row
@@ -236,8 +248,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 
     auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
         if (wave >= DW) return;                     // wave-uniform
-        const uint32_t As = smem_base + buf * STAGE;
-        const uint32_t Bs = As + A_BYTES;
+        const uint32_t As = smem_base + buf * A_BYTES;
+        const uint32_t Bs = smem_base + B_REGION + buf * B_BYTES;
         const i32x4_t a_rsrc = buffer_rsrc(A + row0 * g.K + (int64_t)kt * BK, a_bytes);
         const i32x4_t b_rsrc = buffer_rsrc(B + (int64_t)kt * BK * g.N + col0, b_bytes);
 #pragma unroll
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
                 for (int h = 0; h < 2; ++h) {
                     const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + e;
                     const int n = wn * WN + j * 32 + 16 * (grp & 1) + 4 * q;
-                    b_off[j][ks][h] = A_BYTES + k * (BN * 2) +
+                    b_off[j][ks][h] = B_REGION + k * (BN * 2) +
                                       (((n >> 3) ^ swb(k)) << 4) + ((n & 7) << 1);
                 }
     }
@@ -285,17 +297,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto load_frags = [&](lds_char *S, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN])
+    auto load_frags = [&](int st, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN])
         __attribute__((always_inline)) {
+        lds_char *const SA = smem + st * A_BYTES, *const SB = smem + st * B_BYTES;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(S + a_off[i][ks]);
+            af[i] = *(__attribute__((address_space(3))) bf16x8_t *)(SA + a_off[i][ks]);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][0]));
+                (__attribute__((address_space(3))) i16x4_t *)(SB + b_off[j][ks][0]));
             i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(S + b_off[j][ks][1]));
+                (__attribute__((address_space(3))) i16x4_t *)(SB + b_off[j][ks][1]));
             i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             bfr[j] = __builtin_bit_cast(bf16x8_t, both);
         }
@@ -335,10 +348,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         if (s < KT) issue(s, s);
     // the bias row of the tile's columns (ldc == 0): one 8-byte load per
     // lane, issued with the first operand loads, so it has arrived by the
-    // epilogue
+    // epilogue; the unrolled loop has no registers to hold it across the
+    // mainloop (it would be spilled), so there it is loaded after the loop,
+    // ahead of the last MFMA slice
     uint2 cb_row = {0u, 0u};
-    if (a.has_c && a.ldc == 0)
-        cb_row = *(const uint2 *)((const uint16_t *)a.C + col0 + (lane % (BN / 4)) * 4);
+    if constexpr (!U2)
+        if (a.has_c && a.ldc == 0)
+            cb_row = *(const uint2 *)((const uint16_t *)a.C + col0 + (lane % (BN / 4)) * 4);
     if constexpr (FW > 0) if (a.fuse_reduce == kFuseOwner) {
         // owner-fused reduce: every other rank's partial of this tile was
         // staged by an earlier launch on the stream (so it is visible
@@ -359,26 +375,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
             __hip_atomic_store(a.flags + (int64_t)tid * g.T + t, 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    for (int kt = 0; kt < KT; ++kt) {
+    static_assert(STAGES == 2, "steps alternate between two stages");
+    auto step = [&](int kt, auto st_tag) __attribute__((always_inline)) {
+        const int ST = st_tag;   // kt % 2: a compile-time constant or a run-time value
         // wait until this wave's DMA for step kt has landed (later steps
         // may stay in flight); the barrier makes every wave's data visible
         // and frees the stage read in step kt-1 for the next issue
         const int ahead = KT - 1 - kt;
         wait_groups<AI + BI, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
         __syncthreads();
-        lds_char *S = smem + (kt % STAGES) * STAGE;
-        load_frags(S, 0, af[0], bfr[0]);
+        load_frags(ST, 0, af[0], bfr[0]);
         if (kt > 0) mfmas(1);   // the previous step's last slice
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+        if (kt + 1 < KT) issue(kt + 1, 1 - ST);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
-            load_frags(S, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+            load_frags(ST, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
             mfmas(ks & 1);
             interleave();
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    if constexpr (U2) {
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
+        }
+        if (kt < KT) step(kt, std::integral_constant<int, 0>{});
+    } else {
+        for (int kt = 0; kt < KT; ++kt) step(kt, kt & 1);
     }
+    if constexpr (U2)
+        if (a.has_c && a.ldc == 0)
+            cb_row = *(const uint2 *)((const uint16_t *)a.C + col0 + (lane % (BN / 4)) * 4);
     if (KT > 0) mfmas(1);   // the last step's last slice
 
     // ---- epilogue: D = alpha*acc (+ beta*C on owned rows), scatter ----
@@ -402,7 +432,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     // The plain epilogue's stripes alternate between the two stages, with
     // rows of BN*4 bytes whose 16-byte chunk c of row rr sits at c ^ (rr %
     // 16): the 16 rows one write covers and the chunks one read covers both
-    // land on distinct banks without padding, so a stripe fits one stage.
+    // land on distinct banks without padding, so a stripe fits one stage
+    // (its A tile, then its B tile).
     // The stage that held step KT-2 is free on arrival (every wave has
     // passed the barrier that followed its last reads of it), so the first
     // stripe needs no barrier before it; the stage of step KT-1 is free
@@ -410,7 +441,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int EP_ROW = BN * 4;
     static_assert(SROWS * EP_ROW <= STAGE, "a stripe fits one stage");
     static_assert(STAGES == 2, "stripes alternate between the two stages");
-    lds_char *const ep_buf[2] = {smem + (KT & 1) * STAGE, smem + ((KT + 1) & 1) * STAGE};
+    // a stripe in stage s: its first A_BYTES / EP_ROW rows in the stage's A
+    // tile, the rest in its B tile
+    constexpr int ROWS_IN_A = A_BYTES / EP_ROW;
+    static_assert(ROWS_IN_A * EP_ROW == A_BYTES, "");
+    const int ep_st[2] = {KT & 1, (KT + 1) & 1};
     const uint16_t *Cp = (const uint16_t *)a.C;
     const float alpha = a.alpha, beta = a.beta;
     const int h4 = 4 * (lane >> 5);
@@ -445,11 +480,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
         for (int i = 0; i < FM; ++i) {
             // stage block i of every wave: stripe rows wm*32 .. +31 hold tile
             // rows wm*WM + i*32 .. +31 across all BN columns
-            lds_char *const buf = ep_buf[i & 1];
+            const int est = ep_st[i & 1];
             // stripe row sr, columns 4c .. 4c+3
             auto at = [&](int sr, int c) __attribute__((always_inline)) {
+                lds_char *const row = sr < ROWS_IN_A
+                                          ? smem + est * A_BYTES + sr * EP_ROW
+                                          : smem + B_REGION + est * B_BYTES +
+                                                (sr - ROWS_IN_A) * EP_ROW;
                 return (__attribute__((address_space(3))) f32x4_t *)(
-                    buf + sr * EP_ROW + ((c ^ (sr & 15)) << 4));
+                    row + ((c ^ (sr & 15)) << 4));
             };
 #pragma unroll
             for (int j = 0; j < FN; ++j)
@@ -787,7 +826,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW = 0>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int FW = 0, bool U2 = false>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
     constexpr size_t lds_bytes = (size_t)STAGES * (BM + BN) * BK * 2;
     static_assert(lds_bytes <= 160 * 1024, "LDS");
@@ -801,12 +840,12 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
         return hipErrorInvalidDevice;
     std::call_once(once[dev], [dev] {
         set_rc[dev] = hipFuncSetAttribute(
-            (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW>,
+            (const void *)gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW, U2>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     });
     if (set_rc[dev] != hipSuccess) return set_rc[dev];
     const int64_t blocks = a.n_blocks;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, STAGES, WGM, WGN, FW, U2>),
                        dim3((unsigned)blocks), dim3(64 * WGM * WGN), lds_bytes, s, a);
     return hipGetLastError();
 }
@@ -832,7 +871,12 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
             return launch_tile<256, 256, BKc, ST, 2, 4, 8>(a, s);
         return hipErrorInvalidValue;
     }
-    if (bm == 256 && bn == 256) return launch_tile<256, 256, BKc, ST, 2, 4>(a, s);
+    if (bm == 256 && bn == 256) {
+        // the unrolled loop unless this launch shares the CUs with another
+        // kernel's waves (all-gather copies: signals; reduce slices: coresident)
+        if (!a.signals && !a.coresident) return launch_tile<256, 256, BKc, ST, 2, 4, 0, true>(a, s);
+        return launch_tile<256, 256, BKc, ST, 2, 4>(a, s);
+    }
     if (bm == 256 && bn == 128) return launch_tile<256, 128, BKc, ST, 2, 2>(a, s);
     if (bm == 128 && bn == 128) return launch_tile<128, 128, BKc, ST, 2, 2>(a, s);
     // 64 x 128 (the m <= 64 decode shard, HBM-bound): four waves of 64 x 32

@@ -273,10 +273,11 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
     // the W virtual ranks share one GPU: run them rank after rank across
     // the XCDs (each rank's own tile order is unchanged)
     a.xcd_rank_major = 1;
-    auto gemm = [&](uint32_t b_lo, uint32_t b_hi, hipStream_t st) {
+    auto gemm = [&](uint32_t b_lo, uint32_t b_hi, hipStream_t st, int coresident = 0) {
         GemmArgs x = a;
         x.b_offset = b_lo;
         x.n_blocks = b_hi - b_lo;
+        x.coresident = coresident;
         // the tabulated slots hold the full launch only
         x.slot_tab = (b_lo == 0 && b_hi == a.n_blocks) ? p->slot_tab : nullptr;
         if (x.n_blocks == 0) return hipSuccess;
@@ -368,7 +369,7 @@ int enqueue(gemm_rs_plan_s *p, const void *A, const void *B, const void *C, floa
         const uint32_t parts = W < (uint32_t)kChunkSlices ? W : (uint32_t)kChunkSlices;
         for (uint32_t j = 0; j < parts && e == hipSuccess; ++j) {
             const uint32_t q0 = n * ((W * j) / parts), q1 = n * ((W * (j + 1)) / parts);
-            e = gemm(W * q0, W * q1, s);
+            e = gemm(W * q0, W * q1, s, 1);
             if (e == hipSuccess) e = hipEventRecord(p->slice_done[j], s);
             if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->slice_done[j], 0);
             if (e == hipSuccess) {

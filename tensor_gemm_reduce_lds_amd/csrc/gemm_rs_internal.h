@@ -232,6 +232,10 @@ struct GemmArgs {
     // A have arrived (bounded by timeout_ticks; a timeout is recorded in err)
     int32_t plain_out;
     const uint32_t *signals;
+    // 1: the launch shares the CUs with another kernel's waves (the
+    // identity-order reduce slices), so it keeps the register budget that
+    // leaves them room (a gated all-gather launch, signals != null, too)
+    int32_t coresident;
     uint32_t epoch;
     uint64_t timeout_ticks;
     int32_t *err;

@@ -40,9 +40,10 @@ def _report(src):
 
 def _params(name):
     """Template arguments of a gemm_bf16_kernel instantiation: BM, BN, BK,
-    STAGES, WGM, WGN and FW (0: plain epilogue, W: owner-fused reduce)."""
+    STAGES, WGM, WGN, FW (0: plain epilogue, W: owner-fused reduce) and U2
+    (1: the K loop unrolled by two steps)."""
     return tuple(map(int, re.search(
-        r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE", name).groups()))
+        r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)EE", name).groups()))
 
 
 def _gemms():
@@ -52,7 +53,8 @@ def _gemms():
 
 def _plain_gemms():
     # the instantiations the all-gather and the overlapped slices run beside
-    return {k: v for k, v in _gemms().items() if _params(k)[6] == 0}
+    # (the rolled K loop; the unrolled one is only launched alone)
+    return {k: v for k, v in _gemms().items() if _params(k)[6] == 0 and _params(k)[7] == 0}
 
 
 def _alloc(vgprs, agprs):
@@ -73,7 +75,7 @@ def test_copy_wave_fits_beside_every_gemm_configuration():
     gemms = _plain_gemms()
     assert len(gemms) == 4
     for name, r in gemms.items():
-        bm, bn, bk, stages, wgm, wgn, _ = _params(name)
+        bm, bn, bk, stages, wgm, wgn, _, _ = _params(name)
         lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
         wgs_per_cu = LDS_PER_CU // lds
         waves_by_lds = -(-wgs_per_cu * wgm * wgn // SIMDS_PER_CU)
@@ -98,7 +100,7 @@ def test_overlap_reduce_slices_fit_beside_every_gemm_configuration():
     need = max(_alloc(v["VGPRs"], v.get("AGPRs", 0)) for v in red.values())
     gemms = _plain_gemms()
     for name, r in gemms.items():
-        bm, bn, bk, stages, wgm, wgn, _ = _params(name)
+        bm, bn, bk, stages, wgm, wgn, _, _ = _params(name)
         lds = stages * (bm + bn) * bk * 2 + r.get("LDS", 0)
         waves = min(r["Occupancy"], -(-(LDS_PER_CU // lds) * wgm * wgn // SIMDS_PER_CU))
         free = VGPRS_PER_SIMD_LANE - waves * _alloc(r["VGPRs"], r.get("AGPRs", 0))
@@ -116,7 +118,23 @@ def test_fused_reduce_variant_keeps_the_plain_occupancy():
     assert fused, "no owner-fused instantiation"
     for name, r in fused.items():
         plain = [v for k, v in gemms.items() if _params(k)[:6] == _params(name)[:6]
-                 and _params(k)[6] == 0]
+                 and _params(k)[6:] == (0, 0)]
         assert len(plain) == 1
         assert r.get("ScratchSize", 0) == 0, name
+        assert r["Occupancy"] >= plain[0]["Occupancy"], (name, r, plain[0])
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC),
+                    reason="hipcc not available")
+def test_unrolled_loop_keeps_the_plain_occupancy():
+    """The K loop unrolled by two steps (stage offsets in the DS reads'
+    immediate fields) exists for the 256 x 256 plain kernel only and keeps
+    its two workgroup waves per SIMD."""
+    gemms = _gemms()
+    unrolled = {k: v for k, v in gemms.items() if _params(k)[7] == 1}
+    assert [_params(k)[:7] for k in unrolled] == [(256, 256, 64, 2, 2, 4, 0)]
+    for name, r in unrolled.items():
+        plain = [v for k, v in gemms.items() if _params(k)[:6] == _params(name)[:6]
+                 and _params(k)[6:] == (0, 0)]
+        assert len(plain) == 1
         assert r["Occupancy"] >= plain[0]["Occupancy"], (name, r, plain[0])
