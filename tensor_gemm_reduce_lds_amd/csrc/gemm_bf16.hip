@@ -189,7 +189,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
-    if (a.signals) {
+    // (the unrolled instantiation is never launched gated: without the
+    // gate's workgroup vote it holds no static LDS, its dynamic LDS starts
+    // at address 0, and every fragment address folds into the reads'
+    // immediate offsets)
+    if constexpr (!U2) if (a.signals) {
         // all-gather mode: wait until this tile-row of A has been copied in
         // (agent-scope acquire, bounded); the loads below then see it
         int failed = 0;
